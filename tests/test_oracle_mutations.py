@@ -1,0 +1,96 @@
+"""Planted mistakes in the oracle (on the CPU only) must each fail a pin.
+
+Each case copies an oracle module's source, applies one plausible slip — a
+swapped index, a dropped term, a flipped sign, a wrong operand — loads the
+copy as a throwaway module and runs the pins against it."""
+import os
+import types
+
+import pytest
+
+import test_oracle_allocator as TAL
+import test_oracle_attention as TA
+import test_oracle_cache_write as TC
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _mutant(rel, old, new):
+    path = os.path.join(ROOT, rel)
+    src = open(path).read()
+    assert src.count(old) >= 1, (rel, old)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new, 1), path, "exec"), mod.__dict__)
+    return mod
+
+
+def _caught(pins, *args):
+    for pin in pins:
+        try:
+            pin(*args)
+        except (Exception, pytest.fail.Exception):
+            return True
+    return False
+
+
+ATTN = [
+    ("cache[int(table_row[t // block_size]), t % block_size]",
+     "cache[int(table_row[t % block_size]), t // block_size]"),
+    ("g = h // group", "g = h % group"),
+    ("logits = scale * (k @ q)", "logits = (k @ q)"),
+    ("return e / e.sum(axis=-1, keepdims=True)", "return e"),
+    ("softmax_weights(logits) @ v", "softmax_weights(-logits) @ v"),
+    ("softmax_weights(logits) @ v", "softmax_weights(logits) @ k"),
+    ("<< 16", "<< 15"),
+    ("for t in range(ctx)]", "for t in range(ctx - 1)]"),
+    ("attend(qf[b, h], k[:, g, :], v[:, g, :], scale)", "attend(qf[b, h], k[:, g, :], v[:, 0, :], scale)"),
+    ("attend(qf[b, h], k[:, g, :], v[:, g, :], scale)", "attend(qf[b, g], k[:, g, :], v[:, g, :], scale)"),
+    ("z = logits - logits.max(axis=-1, keepdims=True)", "z = logits - logits.max(axis=-1, keepdims=True) * 0 + 1e-3 * logits"),
+    ("return np.zeros(q_bh.shape[-1], dtype=np.float64)", "return np.ones(q_bh.shape[-1], dtype=np.float64)"),
+    ("np.asarray(x, dtype=np.float32).astype(np.float64)", "np.asarray(x, dtype=np.float16).astype(np.float64)"),
+]
+
+
+@pytest.mark.parametrize("old,new", ATTN, ids=[f"attn{i}" for i in range(len(ATTN))])
+def test_attention_mutant_caught(old, new):
+    assert _caught(TA.PINS, _mutant("oracle/attention.py", old, new))
+
+
+CW = [
+    ("kc[slot // bs, slot % bs] = key[i]", "kc[slot % bs, slot // bs] = key[i]"),
+    ("vc[slot // bs, slot % bs] = value[i]", "vc[slot // bs, slot % bs] = key[i]"),
+    ("if slot < 0:\n            continue", "if slot < -1:\n            continue"),
+    ("kc = k_cache.copy()", "kc = k_cache"),
+]
+
+
+@pytest.mark.parametrize("old,new", CW, ids=[f"cw{i}" for i in range(len(CW))])
+def test_cache_write_mutant_caught(old, new):
+    assert _caught(TC.PINS, _mutant("oracle/cache_write.py", old, new))
+
+
+ALLOC = [
+    ("return (num_tokens + block_size - 1) // block_size", "return num_tokens // block_size"),
+    ("return int(table[pos // block_size]) * block_size + pos % block_size",
+     "return int(table[pos // block_size]) * block_size + pos // block_size"),
+    ("blk = self.free.popleft()", "blk = self.free.pop()"),
+    ("self.free.append(blk)", "self.free.appendleft(blk)"),
+    ("if pos % bs == 0:", "if pos % bs == 1:"),
+    ("self.refcount[blk] -= 1", "self.refcount[blk] -= 2"),
+    ("if n and length % bs and self.refcount[table[-1]] > 1:", "if n and length % bs and self.refcount[table[-1]] > 2:"),
+    ("if need > len(self.free):", "if need > len(self.free) + 1:"),
+    ("shared = self.tables[src][: blocks_for(num_tokens, bs)]", "shared = self.tables[src][: num_tokens // bs]"),
+    ("tables[i, : len(t)] = t", "tables[i, : len(t)] = t[::-1]"),
+]
+
+ALLOC_PINS = ["test_worked_example_960_vs_16384", "test_block_lookup_example",
+              "test_fifo_policy_and_free_order", "test_errors_leave_state_unchanged",
+              "test_shared_write_refused", "test_build_block_tables",
+              "test_invariants_random_ops", "test_workload_replay_shapes"]
+
+
+@pytest.mark.parametrize("old,new", ALLOC, ids=[f"alloc{i}" for i in range(len(ALLOC))])
+def test_allocator_mutant_caught(old, new, monkeypatch):
+    m = _mutant("oracle/allocator.py", old, new)
+    monkeypatch.setattr(TAL, "OAL", m)
+    assert _caught([getattr(TAL, n) for n in ALLOC_PINS])
