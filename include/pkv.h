@@ -1,0 +1,235 @@
+/*
+ * pkv.h — C ABI of libpkv, PagedAttention decode for AMD MI355X (gfx950).
+ *
+ * The operations follow the pages' statement of the method:
+ *   - "vLLM in Production — PagedAttention, Continuous Batching, and
+ *     OpenAI-Compatible LLM Serving" (datasops.com), section
+ *     "PagedAttention — Virtual Memory for the KV Cache": each sequence's
+ *     keys and values live in fixed-size blocks anywhere in GPU memory; a
+ *     per-sequence block table maps logical blocks to physical ones and grows
+ *     one block at a time as tokens arrive;
+ *   - "Serving models with vLLM" (allaboutaibydeep.pages.dev), section
+ *     "How it works: PagedAttention": blocks are allocated on demand, only a
+ *     sequence's last block is partly empty, and sequences with a common
+ *     prefix can point at the same physical blocks;
+ *   - "What Is vLLM: The Fast Inference Engine for Large Language Models"
+ *     (fp8.co), section "How does PagedAttention work?": attention for a
+ *     position looks up the physical block holding that position and indexes
+ *     into it; shared blocks are tracked by reference counts.
+ *
+ * Conventions for every call:
+ *   - Device pointers are owned by the caller (typically torch tensors on the
+ *     current device) and must stay valid until the work queued on `stream`
+ *     has finished.  `stream` is a hipStream_t (NULL = the null stream).
+ *   - GPU calls are asynchronous on `stream`; they never allocate, free or
+ *     synchronize device memory.
+ *   - Every call returns a status.  Arguments are validated on the host
+ *     before anything is launched; a failing call launches nothing and leaves
+ *     all state unchanged.  pkv_last_error() gives a message for the last
+ *     non-OK status returned on the calling thread.
+ *   - Element types: PKV_F32 (float32) or PKV_BF16 (bfloat16).  q, caches,
+ *     new keys/values and the attention output all share one element type.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,  /* a pointer, size or id is out of range          */
+  PKV_ERR_UNSUPPORTED = -2,  /* valid but not built (head_dim, block size ...) */
+  PKV_ERR_OUT_OF_BLOCKS = -3,/* the pool has too few free blocks               */
+  PKV_ERR_NOT_FOUND = -4,    /* unknown sequence id                            */
+  PKV_ERR_SHARED_WRITE = -5, /* append into a block another sequence holds     */
+  PKV_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required     */
+  PKV_ERR_HIP = -7           /* a HIP runtime call or kernel launch failed     */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------
+ * Cache write: store new tokens' keys and values through a slot mapping.
+ *
+ * Token i's rows key[i] and value[i] (each [num_kv_heads, head_dim]) go to
+ * row (slot % block_size) of physical block (slot / block_size), where
+ * slot = slot_mapping[i] was handed out by the block allocator for that
+ * token's position.  A negative slot marks a padding token and is skipped;
+ * so is a slot >= num_blocks * block_size.  Slots in one call must be
+ * distinct (the allocator never repeats one).  All other cache bytes are
+ * left untouched; the copy is bit-exact.
+ *
+ * key, value    device, [num_tokens, num_kv_heads, head_dim], rows of token i
+ *               start at i * key_token_stride / i * value_token_stride
+ *               elements (pass num_kv_heads * head_dim when contiguous);
+ *               the [num_kv_heads, head_dim] part is contiguous.
+ * k_cache,
+ * v_cache       device, [num_blocks, block_size, num_kv_heads, head_dim],
+ *               contiguous, written in place.
+ * slot_mapping  device, int64 [num_tokens].
+ * Supported: head_dim in {64, 128}; num_tokens >= 0 (0 launches nothing).
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_kv_reshape_and_cache(const void* key, const void* value,
+                                    void* k_cache, void* v_cache,
+                                    const int64_t* slot_mapping,
+                                    int32_t num_tokens, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks,
+                                    int64_t key_token_stride,
+                                    int64_t value_token_stride,
+                                    pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention: one query token per sequence.
+ *
+ * For sequence b and query head h (kv head g = h / (num_q_heads /
+ * num_kv_heads)): out[b, h] = softmax(scale * K_b q[b, h]) V_b, where K_b
+ * and V_b are the context_lens[b] rows of kv head g gathered through the
+ * block table: token t sits in block block_tables[b, t / block_size] at
+ * row t % block_size.  Every token attends to its whole context (no other
+ * mask).  context_lens[b] == 0 gives an all-zero output row.  Softmax and
+ * the weighted sum accumulate in float32; the output is rounded to the
+ * element type (nearest-even for bf16).
+ *
+ * With partition_size > 0 each sequence is cut into partitions of that
+ * many tokens, handled in parallel, then merged by a log-sum-exp reduction;
+ * the result equals the single-pass one up to rounding.
+ * partition_size == 0: single pass per sequence.
+ * partition_size == PKV_PARTITION_AUTO (-1): the library chooses.
+ *
+ * out           device, [num_seqs, num_q_heads, head_dim].
+ * q             device, [num_seqs, num_q_heads, head_dim].
+ * k_cache,
+ * v_cache       device, [num_blocks, block_size, num_kv_heads, head_dim].
+ * block_tables  device, int32 [num_seqs, max_blocks_per_seq]; entries past
+ *               a sequence's last block are never read; ids must lie in
+ *               [0, num_blocks) (an id outside reads block 0 rather than
+ *               faulting, and the result is meaningless).
+ * context_lens  device, int32 [num_seqs]; each value is clamped to
+ *               [0, min(max_context_len, max_blocks_per_seq * block_size)].
+ * max_context_len  host-side upper bound of context_lens (sizes the grid).
+ * workspace     device scratch of at least pkv_decode_workspace_bytes(...)
+ *               bytes when partitions are used (may be NULL otherwise).
+ * Supported: head_dim in {64, 128}; block_size in {16, 32};
+ *            num_q_heads a multiple of num_kv_heads with a group of at most
+ *            16; partition_size a multiple of block_size (or 0 / -1);
+ *            num_seqs <= 65535.
+ * ---------------------------------------------------------------------- */
+#define PKV_PARTITION_AUTO (-1)
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_context_len,
+                                  int32_t partition_size, pkv_dtype dtype);
+
+/* The partition size the library uses for these arguments (resolves AUTO);
+ * 0 means single pass. */
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_context_len,
+                                  int32_t partition_size, pkv_dtype dtype);
+
+pkv_status pkv_paged_attention_decode(void* out, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens,
+                                      int32_t max_context_len, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, float scale,
+                                      int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, pkv_dtype dtype,
+                                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block copy: cache[dst] = cache[src] for each (src, dst) pair, K and V.
+ * Used to give a sequence a private copy of a block that others still hold
+ * (copy-on-write of a shared block, "What Is vLLM …", section "How does
+ * PagedAttention work?", memory-sharing step).
+ * pairs  device, int64 [num_pairs, 2] as (src, dst); ids outside
+ *        [0, num_blocks) are skipped; a dst must not appear twice nor be
+ *        any pair's src.
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
+                           int32_t num_pairs, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_dim, pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator (host memory only; single-threaded use).
+ *
+ * Fixed-size blocks are handed out one at a time as a sequence grows; a
+ * sequence's table lists its physical blocks in logical order and token
+ * pos is stored at slot table[pos / block_size] * block_size +
+ * pos % block_size.  Free blocks are handed out first-in first-out,
+ * starting from free_order (a permutation of 0..num_blocks-1, or ascending
+ * when NULL); a freed block joins the tail when its reference count drops
+ * to zero.  Forked sequences share blocks by reference count.
+ * ---------------------------------------------------------------------- */
+typedef struct pkv_allocator pkv_allocator;
+
+/* Creates an allocator; *out receives the handle (library-owned memory,
+ * released by pkv_allocator_destroy). */
+pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_size,
+                                const int32_t* free_order, pkv_allocator** out);
+void pkv_allocator_destroy(pkv_allocator* a);
+
+/* New empty sequence; PKV_ERR_INVALID_ARG if the id exists. */
+pkv_status pkv_seq_add(pkv_allocator* a, int64_t seq_id);
+
+/* dst (existing, empty) shares the blocks holding src's first num_tokens
+ * tokens (each block's reference count + 1).  num_tokens must be a multiple
+ * of block_size or src's whole length. */
+pkv_status pkv_seq_fork_prefix(pkv_allocator* a, int64_t src, int64_t dst,
+                               int32_t num_tokens);
+
+/* Grows seq_id by num_tokens; slots_out (host, int64 [num_tokens], may be
+ * NULL) receives their slots.  PKV_ERR_OUT_OF_BLOCKS if the pool is short,
+ * PKV_ERR_SHARED_WRITE if a token would land in a block another sequence
+ * holds; both leave the allocator unchanged. */
+pkv_status pkv_seq_append(pkv_allocator* a, int64_t seq_id, int32_t num_tokens,
+                          int64_t* slots_out);
+
+/* Batched append: sequence seq_ids[i] grows by num_tokens[i], in order;
+ * slots_out (host, int64 [sum of num_tokens]) receives all new slots in
+ * that order.  All-or-nothing. */
+pkv_status pkv_append_tokens(pkv_allocator* a, const int64_t* seq_ids,
+                             const int32_t* num_tokens, int32_t num_seqs,
+                             int64_t* slots_out);
+
+/* Releases the sequence; blocks whose count drops to zero are freed. */
+pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id);
+
+/* tables_out (host, int32 [num_seqs, max_blocks_per_seq]) receives each
+ * sequence's block table padded with pad_value; context_lens_out (host,
+ * int32 [num_seqs], may be NULL) their lengths.  PKV_ERR_INVALID_ARG if a
+ * sequence has more than max_blocks_per_seq blocks. */
+pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64_t* seq_ids,
+                                  int32_t num_seqs, int32_t max_blocks_per_seq,
+                                  int32_t pad_value, int32_t* tables_out,
+                                  int32_t* context_lens_out);
+
+int32_t pkv_num_free_blocks(const pkv_allocator* a);
+/* Reference count of a block (0 = free), -1 for an id outside the pool. */
+int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block_id);
+/* Length in tokens of a sequence, -1 if unknown. */
+int64_t pkv_seq_context_len(const pkv_allocator* a, int64_t seq_id);
+/* Number of blocks of a sequence, -1 if unknown. */
+int32_t pkv_seq_num_blocks(const pkv_allocator* a, int64_t seq_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

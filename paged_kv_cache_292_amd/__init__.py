@@ -1,0 +1,257 @@
+"""PagedAttention decode for AMD MI355X (gfx950): Python binding of libpkv.
+
+Thin ctypes marshalling over the C ABI declared in ``include/pkv.h``; every
+step of the hot path runs in the library's HIP kernels or its C++ allocator.
+Device arguments are torch tensors (their ``data_ptr()``), launched on the
+current torch stream unless a stream is given.  The library must be built
+first (``python -m paged_kv_cache_292_amd.build``); importing this package
+without it raises ``ImportError`` — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "LIB_PATH", "lib", "PkvError", "F32", "BF16", "PARTITION_AUTO",
+    "kv_reshape_and_cache", "paged_attention_decode", "decode_workspace_bytes",
+    "decode_partition_size", "copy_blocks", "Allocator", "EXPORTS", "version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+F32 = 0
+BF16 = 1
+PARTITION_AUTO = -1
+
+STATUS = {
+    0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "OUT_OF_BLOCKS", -4: "NOT_FOUND",
+    -5: "SHARED_WRITE", -6: "WORKSPACE", -7: "HIP",
+}
+
+# name -> (restype, argtypes), the exported C ABI
+_i32, _i64, _sz, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+_P = ctypes.POINTER
+EXPORTS = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_kv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _i64, _i64, _i32, _vp]),
+    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
+                                          _vp]),
+    "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_allocator_create": (_i32, [_i32, _i32, _P(_i32), _P(_vp)]),
+    "pkv_allocator_destroy": (None, [_vp]),
+    "pkv_seq_add": (_i32, [_vp, _i64]),
+    "pkv_seq_fork_prefix": (_i32, [_vp, _i64, _i64, _i32]),
+    "pkv_seq_append": (_i32, [_vp, _i64, _i32, _P(_i64)]),
+    "pkv_append_tokens": (_i32, [_vp, _P(_i64), _P(_i32), _i32, _P(_i64)]),
+    "pkv_seq_free": (_i32, [_vp, _i64]),
+    "pkv_build_block_tables": (_i32, [_vp, _P(_i64), _i32, _i32, _i32, _P(_i32), _P(_i32)]),
+    "pkv_num_free_blocks": (_i32, [_vp]),
+    "pkv_block_refcount": (_i32, [_vp, _i32]),
+    "pkv_seq_context_len": (_i64, [_vp, _i64]),
+    "pkv_seq_num_blocks": (_i32, [_vp, _i64]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m paged_kv_cache_292_amd.build`")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.code = STATUS.get(status, str(status))
+        msg = lib.pkv_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {self.code}: {msg}")
+
+
+def _check(st: int, where: str) -> None:
+    if st != 0:
+        raise PkvError(st, where)
+
+
+def version() -> str:
+    return lib.pkv_version().decode()
+
+
+# ------------------------------------------------------------------ device calls
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def kv_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """Write ``key``/``value`` ``[T, Hkv, D]`` into the caches at ``slot_mapping`` (int64)."""
+    N, bs, Hkv, D = k_cache.shape
+    T = key.shape[0]
+    _check(lib.pkv_kv_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        slot_mapping.data_ptr(), T, Hkv, D, bs, N,
+        key.stride(0) if T else Hkv * D, value.stride(0) if T else Hkv * D,
+        _dtype_code(k_cache), _stream_ptr(stream)), "kv_reshape_and_cache")
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, partition_size=PARTITION_AUTO, dtype=BF16) -> int:
+    return int(lib.pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len, partition_size,
+                                              dtype))
+
+
+def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_context_len, partition_size=PARTITION_AUTO, dtype=BF16) -> int:
+    return int(lib.pkv_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             block_size, max_context_len, partition_size, dtype))
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len: int, scale: float,
+                           partition_size: int = PARTITION_AUTO, workspace=None,
+                           stream=None) -> None:
+    """``out[b, h] = softmax(scale · K_b q[b, h]) V_b`` through the block tables.
+
+    ``workspace`` is a device byte tensor of at least
+    ``decode_workspace_bytes(...)`` bytes when partitions are used."""
+    N, bs, Hkv, D = k_cache.shape
+    B, Hq, _ = q.shape
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_decode(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
+        ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode")
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """``cache[dst] = cache[src]`` for each row ``(src, dst)`` of int64 ``pairs [P, 2]``."""
+    N, bs, Hkv, D = k_cache.shape
+    _check(lib.pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(),
+                               pairs.shape[0], N, bs, Hkv, D, _dtype_code(k_cache),
+                               _stream_ptr(stream)), "copy_blocks")
+
+
+# ------------------------------------------------------------------ allocator
+class Allocator:
+    """Host block allocator (C++); see ``pkv_allocator_*`` in ``include/pkv.h``."""
+
+    def __init__(self, num_blocks: int, block_size: int,
+                 free_order: Optional[Sequence[int]] = None):
+        h = ctypes.c_void_p()
+        fo = None
+        if free_order is not None:
+            self._fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            if self._fo.shape != (num_blocks,):
+                raise ValueError("free_order must have num_blocks entries")
+            fo = self._fo.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        _check(lib.pkv_allocator_create(num_blocks, block_size, fo, ctypes.byref(h)),
+               "allocator_create")
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add(self, seq: int) -> None:
+        _check(lib.pkv_seq_add(self._h, seq), "seq_add")
+
+    def fork_prefix(self, src: int, dst: int, num_tokens: int) -> None:
+        _check(lib.pkv_seq_fork_prefix(self._h, src, dst, num_tokens), "seq_fork_prefix")
+
+    def append(self, seq: int, n: int) -> np.ndarray:
+        out = np.empty(max(n, 0), dtype=np.int64)
+        _check(lib.pkv_seq_append(self._h, seq, n,
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))), "seq_append")
+        return out
+
+    def append_tokens(self, seqs: Sequence[int], counts: Sequence[int],
+                      out: Optional[np.ndarray] = None) -> np.ndarray:
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        c = np.ascontiguousarray(counts, dtype=np.int32)
+        total = int(c.sum()) if len(c) else 0
+        if out is None:
+            out = np.empty(total, dtype=np.int64)
+        elif out.dtype != np.int64 or out.size < total or not out.flags.c_contiguous:
+            raise ValueError("out must be a contiguous int64 array large enough")
+        _check(lib.pkv_append_tokens(self._h, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(s),
+                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+               "append_tokens")
+        return out[:total]
+
+    def free(self, seq: int) -> None:
+        _check(lib.pkv_seq_free(self._h, seq), "seq_free")
+
+    def build_block_tables(self, seqs: Sequence[int], max_blocks: int, pad: int = -1,
+                           tables_out: Optional[np.ndarray] = None,
+                           ctx_out: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        t = tables_out if tables_out is not None else np.empty((len(s), max_blocks), np.int32)
+        c = ctx_out if ctx_out is not None else np.empty(len(s), np.int32)
+        if t.dtype != np.int32 or t.shape != (len(s), max_blocks) or not t.flags.c_contiguous:
+            raise ValueError("tables_out must be a contiguous int32 [num_seqs, max_blocks]")
+        _check(lib.pkv_build_block_tables(self._h, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                          len(s), max_blocks, pad,
+                                          t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                          c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+               "build_block_tables")
+        return t, c
+
+    def num_free_blocks(self) -> int:
+        return int(lib.pkv_num_free_blocks(self._h))
+
+    def block_refcount(self, block: int) -> int:
+        return int(lib.pkv_block_refcount(self._h, block))
+
+    def context_len(self, seq: int) -> int:
+        return int(lib.pkv_seq_context_len(self._h, seq))
+
+    def num_blocks_of(self, seq: int) -> int:
+        return int(lib.pkv_seq_num_blocks(self._h, seq))
+
+    def replay(self, ops: Iterable[tuple]) -> None:
+        """Run a workload's op list (``add`` / ``append`` / ``fork``)."""
+        for op in ops:
+            if op[0] == "add":
+                self.add(op[1])
+            elif op[0] == "append":
+                self.append(op[1], op[2])
+            elif op[0] == "fork":
+                self.fork_prefix(op[1], op[2], op[3])
+            else:
+                raise ValueError(op)

@@ -1,0 +1,222 @@
+// Host block allocator for the paged KV cache.
+//
+// Fixed-size blocks are handed out one at a time as sequences grow, and each
+// sequence keeps a table of its physical blocks in logical order ("vLLM in
+// Production …", section "PagedAttention — Virtual Memory for the KV Cache";
+// "Serving models with vLLM", section "How it works: PagedAttention").
+// Sequences with a common prefix share physical blocks, tracked by reference
+// counts ("What Is vLLM …", section "How does PagedAttention work?").
+//
+// Policy where the pages are silent: free blocks leave a FIFO queue that
+// starts as the caller's free_order; a block whose count drops to zero joins
+// its tail.  Every operation checks all of its preconditions before changing
+// anything, so a failing call leaves the allocator as it was.
+#include <cstdint>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv_internal.h"
+
+struct pkv_allocator {
+  struct Seq {
+    std::vector<int32_t> blocks;
+    int64_t len = 0;
+  };
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::deque<int32_t> free_q;
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int64_t blocks_for(int64_t tokens) const {
+    return (tokens + block_size - 1) / block_size;
+  }
+  // Whether appending n > 0 tokens to s would write into a block that another
+  // sequence also holds (its last block, partly filled and shared).
+  bool writes_shared(const Seq& s, int64_t n) const {
+    return n > 0 && s.len % block_size != 0 && refcount[s.blocks.back()] > 1;
+  }
+  // Appends n tokens (preconditions already checked), writing slots.
+  void grow(Seq& s, int64_t n, int64_t* slots) {
+    for (int64_t pos = s.len; pos < s.len + n; ++pos) {
+      if (pos % block_size == 0) {
+        int32_t blk = free_q.front();
+        free_q.pop_front();
+        refcount[blk] += 1;
+        s.blocks.push_back(blk);
+      }
+      if (slots)
+        *slots++ = int64_t(s.blocks[pos / block_size]) * block_size + pos % block_size;
+    }
+    s.len += n;
+  }
+};
+
+using pkv::fail;
+
+extern "C" pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_size,
+                                           const int32_t* free_order,
+                                           pkv_allocator** out) {
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "allocator_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks < 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "allocator_create: num_blocks=%d block_size=%d",
+                num_blocks, block_size);
+  if (free_order) {
+    std::vector<char> seen(size_t(num_blocks), 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[size_t(b)])
+        return fail(PKV_ERR_INVALID_ARG,
+                    "allocator_create: free_order is not a permutation (entry %d = %d)", i, b);
+      seen[size_t(b)] = 1;
+    }
+  }
+  auto* a = new (std::nothrow) pkv_allocator();
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "allocator_create: out of host memory");
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->refcount.assign(size_t(num_blocks), 0);
+  for (int32_t i = 0; i < num_blocks; ++i) a->free_q.push_back(free_order ? free_order[i] : i);
+  *out = a;
+  return pkv::ok();
+}
+
+extern "C" void pkv_allocator_destroy(pkv_allocator* a) { delete a; }
+
+extern "C" pkv_status pkv_seq_add(pkv_allocator* a, int64_t seq_id) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "seq_add: NULL allocator");
+  if (a->seqs.count(seq_id)) return fail(PKV_ERR_INVALID_ARG, "seq_add: sequence %lld exists", (long long)seq_id);
+  a->seqs.emplace(seq_id, pkv_allocator::Seq{});
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_seq_fork_prefix(pkv_allocator* a, int64_t src, int64_t dst,
+                                          int32_t num_tokens) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "seq_fork_prefix: NULL allocator");
+  auto is = a->seqs.find(src);
+  auto id = a->seqs.find(dst);
+  if (is == a->seqs.end() || id == a->seqs.end())
+    return fail(PKV_ERR_NOT_FOUND, "seq_fork_prefix: unknown sequence (%lld -> %lld)",
+                (long long)src, (long long)dst);
+  const auto& s = is->second;
+  bool whole = num_tokens % a->block_size == 0 || num_tokens == s.len;
+  if (src == dst || num_tokens < 0 || num_tokens > s.len || !whole || id->second.len != 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "seq_fork_prefix: %d tokens of %lld (length %lld) into %lld: needs whole blocks "
+                "or the whole source, and an empty destination",
+                num_tokens, (long long)src, (long long)s.len, (long long)dst);
+  int64_t nb = a->blocks_for(num_tokens);
+  auto& d = id->second;
+  d.blocks.assign(s.blocks.begin(), s.blocks.begin() + nb);
+  for (int32_t b : d.blocks) a->refcount[size_t(b)] += 1;
+  d.len = num_tokens;
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_seq_append(pkv_allocator* a, int64_t seq_id, int32_t num_tokens,
+                                     int64_t* slots_out) {
+  return pkv_append_tokens(a, &seq_id, &num_tokens, 1, slots_out);
+}
+
+extern "C" pkv_status pkv_append_tokens(pkv_allocator* a, const int64_t* seq_ids,
+                                        const int32_t* num_tokens, int32_t num_seqs,
+                                        int64_t* slots_out) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "append: NULL allocator");
+  if (num_seqs < 0 || (num_seqs > 0 && (!seq_ids || !num_tokens)))
+    return fail(PKV_ERR_INVALID_ARG, "append: bad batch (num_seqs=%d)", num_seqs);
+  // Check everything first.  A sequence may appear several times; later
+  // entries see the growth of earlier ones.
+  std::unordered_map<int64_t, int64_t> pending;  // seq -> tokens added so far in this call
+  int64_t need = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PKV_ERR_NOT_FOUND, "append: unknown sequence %lld", (long long)seq_ids[i]);
+    if (num_tokens[i] < 0)
+      return fail(PKV_ERR_INVALID_ARG, "append: negative token count %d", num_tokens[i]);
+    const auto& s = it->second;
+    int64_t& extra = pending[seq_ids[i]];
+    if (extra == 0 && a->writes_shared(s, num_tokens[i]))
+      return fail(PKV_ERR_SHARED_WRITE,
+                  "append: last block of sequence %lld is shared (copy it first)",
+                  (long long)seq_ids[i]);
+    int64_t before = s.len + extra;
+    need += a->blocks_for(before + num_tokens[i]) - a->blocks_for(before);
+    extra += num_tokens[i];
+  }
+  if (need > int64_t(a->free_q.size()))
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "append: need %lld blocks, %zu free", (long long)need,
+                a->free_q.size());
+  int64_t* out = slots_out;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    a->grow(a->seqs[seq_ids[i]], num_tokens[i], out);
+    if (out) out += num_tokens[i];
+  }
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "seq_free: NULL allocator");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end())
+    return fail(PKV_ERR_NOT_FOUND, "seq_free: unknown sequence %lld", (long long)seq_id);
+  for (int32_t b : it->second.blocks) {
+    if (--a->refcount[size_t(b)] == 0) a->free_q.push_back(b);
+  }
+  a->seqs.erase(it);
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64_t* seq_ids,
+                                             int32_t num_seqs, int32_t max_blocks_per_seq,
+                                             int32_t pad_value, int32_t* tables_out,
+                                             int32_t* context_lens_out) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "build_block_tables: NULL allocator");
+  if (num_seqs < 0 || max_blocks_per_seq < 0 ||
+      (num_seqs > 0 && (!seq_ids || (!tables_out && max_blocks_per_seq > 0))))
+    return fail(PKV_ERR_INVALID_ARG, "build_block_tables: bad arguments");
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PKV_ERR_NOT_FOUND, "build_block_tables: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+    if (int64_t(it->second.blocks.size()) > max_blocks_per_seq)
+      return fail(PKV_ERR_INVALID_ARG, "build_block_tables: sequence %lld has %zu blocks > %d",
+                  (long long)seq_ids[i], it->second.blocks.size(), max_blocks_per_seq);
+    if (it->second.len > INT32_MAX)
+      return fail(PKV_ERR_INVALID_ARG, "build_block_tables: sequence too long");
+  }
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const auto& s = a->seqs.at(seq_ids[i]);
+    int32_t* row = tables_out + int64_t(i) * max_blocks_per_seq;
+    size_t n = s.blocks.size();
+    for (size_t j = 0; j < n; ++j) row[j] = s.blocks[j];
+    for (int64_t j = int64_t(n); j < max_blocks_per_seq; ++j) row[j] = pad_value;
+    if (context_lens_out) context_lens_out[i] = int32_t(s.len);
+  }
+  return pkv::ok();
+}
+
+extern "C" int32_t pkv_num_free_blocks(const pkv_allocator* a) {
+  return a ? int32_t(a->free_q.size()) : -1;
+}
+
+extern "C" int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block_id) {
+  if (!a || block_id < 0 || block_id >= a->num_blocks) return -1;
+  return a->refcount[size_t(block_id)];
+}
+
+extern "C" int64_t pkv_seq_context_len(const pkv_allocator* a, int64_t seq_id) {
+  if (!a) return -1;
+  auto it = a->seqs.find(seq_id);
+  return it == a->seqs.end() ? -1 : it->second.len;
+}
+
+extern "C" int32_t pkv_seq_num_blocks(const pkv_allocator* a, int64_t seq_id) {
+  if (!a) return -1;
+  auto it = a->seqs.find(seq_id);
+  return it == a->seqs.end() ? -1 : int32_t(it->second.blocks.size());
+}

@@ -1,0 +1,130 @@
+// Cache writes for gfx950: new tokens' K/V rows through a slot mapping, and
+// whole-block copies.
+//
+// A sequence's cache grows one token at a time; each new token's rows go to
+// the slot the allocator gave its position ("vLLM in Production …", section
+// "PagedAttention — Virtual Memory for the KV Cache").  With the cache laid
+// out [num_blocks][block_size][num_kv_heads][head_dim], slot s = block *
+// block_size + row starts at element s * num_kv_heads * head_dim, so a token
+// is one contiguous copy of num_kv_heads * head_dim elements per cache.
+// Block copies give a sequence its own copy of a block that others still
+// share ("What Is vLLM …", section "How does PagedAttention work?").
+#include <cstdint>
+
+#include "pkv_internal.h"
+#include <hip/hip_runtime.h>
+
+namespace pkv {
+namespace {
+
+// One workgroup per token; 16-byte vectors, K and V interleaved over threads.
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache, const int64_t* __restrict__ slots, int64_t key_stride_vec,
+    int64_t value_stride_vec, int row_vec, int64_t num_slots) {
+  const int i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const uint4* ks = key + i * key_stride_vec;
+  const uint4* vs = value + i * value_stride_vec;
+  uint4* kd = k_cache + slot * row_vec;
+  uint4* vd = v_cache + slot * row_vec;
+  for (int j = threadIdx.x; j < 2 * row_vec; j += blockDim.x) {
+    if (j < row_vec)
+      kd[j] = ks[j];
+    else
+      vd[j - row_vec] = vs[j - row_vec];
+  }
+}
+
+// One workgroup per (pair, cache); copies a whole block.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          const int64_t* __restrict__ pairs,
+                                                          int64_t block_vec, int32_t num_blocks) {
+  const int64_t src = pairs[2 * blockIdx.x];
+  const int64_t dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint4* c = blockIdx.y == 0 ? k_cache : v_cache;
+  const uint4* s = c + src * block_vec;
+  uint4* d = c + dst * block_vec;
+  for (int64_t j = threadIdx.x; j < block_vec; j += blockDim.x) d[j] = s[j];
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" pkv_status pkv_kv_reshape_and_cache(const void* key, const void* value,
+                                               void* k_cache, void* v_cache,
+                                               const int64_t* slot_mapping, int32_t num_tokens,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t num_blocks,
+                                               int64_t key_token_stride,
+                                               int64_t value_token_stride, pkv_dtype dtype,
+                                               void* stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "kv_reshape_and_cache: unknown dtype %d", int(dtype));
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_reshape_and_cache: head_dim=%d (64 or 128)", head_dim);
+  if (num_tokens < 0 || num_kv_heads <= 0 || block_size <= 0 || num_blocks < 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "kv_reshape_and_cache: num_tokens=%d num_kv_heads=%d block_size=%d "
+                "num_blocks=%d", num_tokens, num_kv_heads, block_size, num_blocks);
+  const int64_t esize = dtype == PKV_F32 ? 4 : 2;
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if (key_token_stride < row || value_token_stride < row ||
+      (key_token_stride * esize) % 16 || (value_token_stride * esize) % 16)
+    return fail(PKV_ERR_INVALID_ARG,
+                "kv_reshape_and_cache: token strides (%lld, %lld) must be >= %lld elements "
+                "and multiples of 16 bytes", (long long)key_token_stride,
+                (long long)value_token_stride, (long long)row);
+  if (num_tokens == 0) return pkv::ok();
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "kv_reshape_and_cache: NULL pointer argument");
+  if (!pkv::aligned16(key) || !pkv::aligned16(value) || !pkv::aligned16(k_cache) ||
+      !pkv::aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "kv_reshape_and_cache: tensors must be 16-byte aligned");
+  const int row_vec = int(row * esize / 16);
+  hipLaunchKernelGGL(pkv::reshape_and_cache_kernel, dim3(num_tokens), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(key),
+                     static_cast<const uint4*>(value), static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), slot_mapping, key_token_stride * esize / 16,
+                     value_token_stride * esize / 16, row_vec,
+                     int64_t(num_blocks) * block_size);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "kv_reshape_and_cache: launch failed: %s", hipGetErrorString(e));
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
+                                      int32_t num_pairs, int32_t num_blocks, int32_t block_size,
+                                      int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                                      void* stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: unknown dtype %d", int(dtype));
+  if (num_pairs < 0 || num_pairs > 0x7FFFFFFF || num_blocks < 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: bad sizes");
+  const int64_t esize = dtype == PKV_F32 ? 4 : 2;
+  const int64_t block_bytes = int64_t(block_size) * num_kv_heads * head_dim * esize;
+  if (block_bytes % 16)
+    return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block of %lld bytes is not a multiple of 16",
+                (long long)block_bytes);
+  if (num_pairs == 0) return pkv::ok();
+  if (!k_cache || !v_cache || !pairs)
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: NULL pointer argument");
+  if (!pkv::aligned16(k_cache) || !pkv::aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: caches must be 16-byte aligned");
+  hipLaunchKernelGGL(pkv::copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), pairs, block_bytes / 16, num_blocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "copy_blocks: launch failed: %s", hipGetErrorString(e));
+  return pkv::ok();
+}

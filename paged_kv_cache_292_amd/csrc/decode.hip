@@ -1,0 +1,500 @@
+// Paged decode attention for gfx950.
+//
+// One query token per sequence attends to its whole context, whose keys and
+// values sit in fixed-size blocks reached through the sequence's block table
+// ("vLLM in Production …", section "PagedAttention — Virtual Memory for the
+// KV Cache"; "What Is vLLM …", section "How does PagedAttention work?", the
+// position-to-block lookup).  Cache layout: [num_blocks][block_size]
+// [num_kv_heads][head_dim]; one token's row of one kv head is head_dim
+// contiguous elements.
+//
+// Work split.  A workgroup owns (sequence, kv head, partition).  Its waves
+// take 16-token chunks of the partition round-robin; inside a wave the four
+// 16-lane rows each own one token slot of the chunk and every lane holds
+// head_dim/16 elements of a row, so one 16-byte load per lane fetches four
+// token rows (4 x 256 B for bf16, head_dim 128).  q·k is summed over the 16
+// lanes of a row with DPP; each row keeps its own online-softmax state (max,
+// sum, accumulator) per query head, and rows and waves are merged at the end.
+// The next chunk's K/V loads are issued before the current chunk is reduced.
+//
+// Long contexts are split into partitions handled by separate workgroups;
+// each writes its normalised partial output with its max and sum, and a
+// second kernel merges them by log-sum-exp weights.
+#include <algorithm>
+#include <cfloat>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+using namespace dev;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kChunk = 16;          // tokens per wave iteration
+constexpr int kSingle = 1 << 30;    // "partition" length of single-pass mode
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  float* part_o;   // [B, Hq, max_parts, D]
+  float* part_ml;  // [B, Hq, max_parts, 2] (max in log2 units, sum)
+  int32_t max_blocks;
+  int32_t ctx_cap;  // min(max_context_len, max_blocks * block_size)
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t partition;  // tokens per partition (multiple of 16), kSingle = one
+  int32_t max_parts;
+  float scale_log2;   // scale * log2(e): logits are kept in base-2 units
+};
+
+__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int b) {
+  int c = a.ctx_lens[b];
+  return c < 0 ? 0 : (c > a.ctx_cap ? a.ctx_cap : c);
+}
+
+// ---------------------------------------------------------------------------
+// Partition kernel, query-head group G on the vector ALUs.
+template <typename T, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
+  constexpr int EPL = D / 16;                      // elements per lane
+  constexpr int WORDS = EPL * int(sizeof(T)) / 4;  // 32-bit words per lane
+  using F = Frag<WORDS>;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4;
+  const int r = lane & 15;
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+
+  const int ctx = clamp_ctx(a, b);
+  const int t0 = part * a.partition;
+  const int t1 = min(ctx, t0 + a.partition);
+  const int nparts = (ctx + a.partition - 1) / a.partition;
+  if (t0 >= t1) {
+    if (ctx == 0 && part == 0) {
+      for (int i = threadIdx.x; i < G * D; i += NW * 64)
+        store_elem<T>(a.out, (size_t(b) * Hq + kvh * G) * D + i, 0.0f);
+    }
+    return;
+  }
+
+  // q for the G heads of this kv head, same lane layout as K rows.
+  F qf[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    load_frag(qf[h], static_cast<const T*>(a.q) + (size_t(b) * Hq + kvh * G + h) * D + r * EPL);
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -FLT_MAX;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+  }
+
+  const int row_stride = Hkv * D;  // elements between tokens of one block
+  const T* kc = static_cast<const T*>(a.k_cache);
+  const T* vc = static_cast<const T*>(a.v_cache);
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+  const int c_begin = t0 / kChunk;
+  const int c_end = (t1 + kChunk - 1) / kChunk;
+
+  // Issues the loads of chunk c.  Every lane loads: slots past t1 re-read the
+  // chunk's first row (always inside the context) and are masked to -inf
+  // later, so the loads stay unconditional and the compiler can keep the next
+  // chunk's loads in flight while the current one is reduced.
+  // Per-lane byte offsets of the four slots inside a chunk (loop invariant).
+  uint32_t slot_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    slot_off[i] = uint32_t(((4 * i + grp) * row_stride + r * EPL) * int(sizeof(T)));
+  const uint32_t lane_off = uint32_t(r * EPL * int(sizeof(T)));
+  auto load_chunk = [&](int c, F (&kd)[4], F (&vd)[4]) {
+    const int tc = __builtin_amdgcn_readfirstlane(c * kChunk);  // wave-uniform: scalar loads
+    int bid = scalar_read(tbl + tc / BS);
+    bid = (unsigned)bid < (unsigned)a.num_blocks ? bid : 0;
+    const size_t rowbase = ((size_t(bid) * BS + (tc % BS)) * row_stride + kvh * D) * sizeof(T);
+    const char* kb = reinterpret_cast<const char*>(kc) + rowbase;
+    const char* vb = reinterpret_cast<const char*>(vc) + rowbase;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = tc + 4 * i + grp < t1 ? slot_off[i] : lane_off;
+      load_frag(kd[i], kb + off);
+      load_frag(vd[i], vb + off);
+    }
+  };
+
+  // Online-softmax update of every query head with chunk c's rows.
+  auto consume = [&](int c, const F (&kd)[4], const F (&vd)[4]) {
+    const int tc = c * kChunk;
+    float s[G][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = tc + 4 * i + grp < t1;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.0f;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int w = 0; w < WORDS; ++w) d = dot2_bf16(qf[h].w[w], kd[i].w[w], d);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) d = fmaf(elem<T>(qf[h], e), elem<T>(kd[i], e), d);
+        }
+        d = row_sum16(d) * a.scale_log2;
+        s[h][i] = valid ? d : -INFINITY;
+      }
+    }
+    float vv[4][EPL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vv[i][e] = elem<T>(vd[i], e);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mx = fmaxf(fmaxf(s[h][0], s[h][1]), fmaxf(s[h][2], s[h][3]));
+      const float mn = fmaxf(m[h], mx);
+      const float alpha = fast_exp2(m[h] - mn);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[h][i] - mn);
+      l[h] = l[h] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x = acc[h][e] * alpha;
+        x = fmaf(p[0], vv[0][e], x);
+        x = fmaf(p[1], vv[1][e], x);
+        x = fmaf(p[2], vv[2][e], x);
+        x = fmaf(p[3], vv[3][e], x);
+        acc[h][e] = x;
+      }
+      m[h] = mn;
+    }
+  };
+
+  // Two register buffers, alternating; the prefetch past the last chunk
+  // re-reads the current chunk (a cache hit) so that it needs no branch.
+  F ka[4], va[4], kb2[4], vb2[4];
+  int c = c_begin + wave;
+  if (c < c_end) {
+    load_chunk(c, ka, va);
+    while (true) {
+      int cn = c + NW < c_end ? c + NW : c;
+      load_chunk(cn, kb2, vb2);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+      consume(c, ka, va);
+      c += NW;
+      if (c >= c_end) break;
+      cn = c + NW < c_end ? c + NW : c;
+      load_chunk(cn, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(c, kb2, vb2);
+      c += NW;
+      if (c >= c_end) break;
+    }
+  }
+
+  // Merge the four rows of the wave (lanes r, r+16, r+32, r+48).
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mw = fmaxf(m[h], __shfl_xor(m[h], 16));
+    mw = fmaxf(mw, __shfl_xor(mw, 32));
+    const float f = fast_exp2(m[h] - mw);
+    float lw = l[h] * f;
+    lw += __shfl_xor(lw, 16);
+    lw += __shfl_xor(lw, 32);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = acc[h][e] * f;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[h][e] = x;
+    }
+    m[h] = mw;
+    l[h] = lw;
+  }
+
+  const bool single = nparts == 1;
+  const size_t head0 = size_t(b) * Hq + size_t(kvh) * G;
+  auto finish = [&](int h, int d, float o, float mm, float ll) {
+    if (single) {
+      store_elem<T>(a.out, (head0 + h) * D + d, o / ll);
+    } else {
+      const size_t pi = (head0 + h) * a.max_parts + part;
+      a.part_o[pi * D + d] = o / ll;
+      if (d == 0) {
+        a.part_ml[2 * pi] = mm;
+        a.part_ml[2 * pi + 1] = ll;
+      }
+    }
+  };
+
+  if constexpr (NW == 1) {
+    if (grp == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) finish(h, r * EPL + e, acc[h][e], m[h], l[h]);
+    }
+  } else {
+    __shared__ float s_o[NW][G][D];
+    __shared__ float s_ml[NW][G][2];
+    if (grp == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_o[wave][h][r * EPL + e] = acc[h][e];
+        if (r == 0) {
+          s_ml[wave][h][0] = m[h];
+          s_ml[wave][h][1] = l[h];
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += NW * 64) {
+      const int h = i / D;
+      const int d = i % D;
+      float M = s_ml[0][h][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+      float L = 0.0f, O = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = fast_exp2(s_ml[w][h][0] - M);
+        L = fmaf(s_ml[w][h][1], f, L);
+        O = fmaf(s_o[w][h][d], f, O);
+      }
+      finish(h, d, O, M, L);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of the partitions of one (sequence, query head).
+// out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - max_p m_p).
+template <typename T, int D>
+__global__ __launch_bounds__(64) void reduce_partitions_kernel(DecodeArgs a) {
+  constexpr int DPT = D / 64;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int ctx = clamp_ctx(a, b);
+  const int nparts = (ctx + a.partition - 1) / a.partition;
+  if (nparts <= 1) return;  // written directly by the partition kernel
+  const size_t head = size_t(b) * a.num_q_heads + h;
+  const float* ml = a.part_ml + 2 * head * a.max_parts;
+  const float* po = a.part_o + head * a.max_parts * D;
+  const int t = threadIdx.x;
+
+  float M = -FLT_MAX;
+  for (int p = t; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+
+  float L = 0.0f;
+  float O[DPT];
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) O[j] = 0.0f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+    L += w;
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) O[j] = fmaf(w, po[size_t(p) * D + j * 64 + t], O[j]);
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) store_elem<T>(a.out, head * D + j * 64 + t, O[j] * inv);
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+constexpr int kNW = 4;
+
+template <typename T, int D, int BS, int G>
+hipError_t launch_valu(const DecodeArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
+  dim3 grid(grid_parts, a.num_kv_heads, num_seqs);
+  hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kNW>), grid, dim3(kNW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int BS>
+hipError_t dispatch_group(const DecodeArgs& a, int G, int num_seqs, hipStream_t st,
+                          int grid_parts) {
+  switch (G) {
+    case 1: return launch_valu<T, D, BS, 1>(a, num_seqs, st, grid_parts);
+    case 2: return launch_valu<T, D, BS, 2>(a, num_seqs, st, grid_parts);
+    case 4: return launch_valu<T, D, BS, 4>(a, num_seqs, st, grid_parts);
+    case 8: return launch_valu<T, D, BS, 8>(a, num_seqs, st, grid_parts);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+hipError_t dispatch_bs(const DecodeArgs& a, int BS, int G, int num_seqs, hipStream_t st,
+                       int grid_parts) {
+  return BS == 16 ? dispatch_group<T, D, 16>(a, G, num_seqs, st, grid_parts)
+                  : dispatch_group<T, D, 32>(a, G, num_seqs, st, grid_parts);
+}
+
+template <typename T, int D>
+hipError_t launch_reduce(const DecodeArgs& a, int num_seqs, hipStream_t st) {
+  hipLaunchKernelGGL((reduce_partitions_kernel<T, D>), dim3(a.num_q_heads, num_seqs), dim3(64),
+                     0, st, a);
+  return hipGetLastError();
+}
+
+bool group_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Partition length actually used, 0 = single pass.  AUTO splits long
+// contexts into 512-token partitions.
+int32_t resolve_partition(int32_t max_context_len, int32_t partition_size) {
+  if (partition_size == PKV_PARTITION_AUTO) return max_context_len > 1024 ? 512 : 0;
+  return partition_size;
+}
+
+size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                     int32_t max_context_len, int32_t partition) {
+  if (partition <= 0 || max_context_len <= 0) return 0;
+  const size_t parts = size_t((int64_t(max_context_len) + partition - 1) / partition);
+  const size_t heads = size_t(num_seqs) * size_t(num_q_heads);
+  return heads * parts * (size_t(head_dim) + 2) * sizeof(float);
+}
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" int32_t pkv_decode_partition_size(int32_t, int32_t, int32_t, int32_t, int32_t,
+                                             int32_t max_context_len, int32_t partition_size,
+                                             pkv_dtype) {
+  return pkv::resolve_partition(max_context_len, partition_size);
+}
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_context_len,
+                                             int32_t partition_size, pkv_dtype dtype) {
+  (void)num_kv_heads;
+  (void)block_size;
+  (void)dtype;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return pkv::workspace_for(num_seqs, num_q_heads, head_dim, max_context_len,
+                            pkv::resolve_partition(max_context_len, partition_size));
+}
+
+extern "C" pkv_status pkv_paged_attention_decode(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+    void* stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: unknown dtype %d", int(dtype));
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: num_seqs=%d outside [0, 65535]",
+                num_seqs);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_kv_heads > 65535 ||
+      num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "paged_attention_decode: num_q_heads=%d must be a positive multiple of "
+                "num_kv_heads=%d", num_q_heads, num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: head_dim=%d (64 or 128)", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: block_size=%d (16 or 32)",
+                block_size);
+  if (!pkv::group_supported(G))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "paged_attention_decode: query heads per kv head = %d (1, 2, 4 or 8)", G);
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      max_context_len > (1 << 29))
+    return fail(PKV_ERR_INVALID_ARG,
+                "paged_attention_decode: num_blocks=%d max_blocks_per_seq=%d "
+                "max_context_len=%d", num_blocks, max_blocks_per_seq, max_context_len);
+  if (int64_t(num_seqs) * max_blocks_per_seq > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: block table too large");
+  if (partition_size < PKV_PARTITION_AUTO ||
+      (partition_size > 0 && partition_size % block_size != 0))
+    return fail(PKV_ERR_INVALID_ARG,
+                "paged_attention_decode: partition_size=%d must be 0, -1 or a multiple of "
+                "block_size=%d", partition_size, block_size);
+  if (num_seqs == 0) return pkv::ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: NULL pointer argument");
+
+  const int32_t partition = pkv::resolve_partition(max_context_len, partition_size);
+  const int32_t cap = int32_t(std::min<int64_t>(max_context_len,
+                                                int64_t(max_blocks_per_seq) * block_size));
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.tables = block_tables;
+  a.ctx_lens = context_lens;
+  a.max_blocks = max_blocks_per_seq;
+  a.ctx_cap = cap;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * pkv::kLog2e;
+  int grid_parts = 1;
+  if (partition > 0) {
+    const size_t need = pkv::workspace_for(num_seqs, num_q_heads, head_dim, max_context_len,
+                                           partition);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(PKV_ERR_WORKSPACE,
+                  "paged_attention_decode: workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : size_t(0));
+    a.partition = partition;
+    // the workspace is sized from max_context_len; partitions past the clamped
+    // context are never launched
+    a.max_parts = int32_t((int64_t(max_context_len) + partition - 1) / partition);
+    if (a.max_parts < 1) a.max_parts = 1;
+    float* ws = static_cast<float*>(workspace);
+    a.part_o = ws;
+    a.part_ml = ws + size_t(num_seqs) * num_q_heads * a.max_parts * head_dim;
+    grid_parts = int((int64_t(cap) + partition - 1) / partition);
+    if (grid_parts < 1) grid_parts = 1;
+  } else {
+    a.partition = pkv::kSingle;
+    a.max_parts = 1;
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const bool f32 = dtype == PKV_F32;
+  if (head_dim == 64) {
+    e = f32 ? pkv::dispatch_bs<float, 64>(a, block_size, G, num_seqs, st, grid_parts)
+            : pkv::dispatch_bs<uint16_t, 64>(a, block_size, G, num_seqs, st, grid_parts);
+  } else {
+    e = f32 ? pkv::dispatch_bs<float, 128>(a, block_size, G, num_seqs, st, grid_parts)
+            : pkv::dispatch_bs<uint16_t, 128>(a, block_size, G, num_seqs, st, grid_parts);
+  }
+  if (e == hipSuccess && partition > 0) {
+    if (head_dim == 64)
+      e = f32 ? pkv::launch_reduce<float, 64>(a, num_seqs, st)
+              : pkv::launch_reduce<uint16_t, 64>(a, num_seqs, st);
+    else
+      e = f32 ? pkv::launch_reduce<float, 128>(a, num_seqs, st)
+              : pkv::launch_reduce<uint16_t, 128>(a, num_seqs, st);
+  }
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "paged_attention_decode: launch failed: %s", hipGetErrorString(e));
+  return pkv::ok();
+}

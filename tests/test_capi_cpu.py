@@ -1,0 +1,220 @@
+"""CPU checks of libpkv: it loads, exports every symbol include/pkv.h declares,
+its host allocator matches the oracle allocator bit for bit, and its argument
+checks reject bad calls before anything reaches the GPU."""
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle.allocator as OAL
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+P = pytest.importorskip("paged_kv_cache_292_amd", reason="libpkv.so not built")
+
+
+def _declared():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names.update(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared()
+    assert {"pkv_paged_attention_decode", "pkv_kv_reshape_and_cache",
+            "pkv_allocator_create", "pkv_build_block_tables"} <= declared
+    for name in declared:
+        assert hasattr(P.lib, name), name
+    assert declared == set(P.EXPORTS), declared ^ set(P.EXPORTS)
+    assert "gfx950" in P.version()
+
+
+# ------------------------------------------------------------------ allocator parity
+def _both(n, bs, free_order=None):
+    return OAL.BlockAllocator(n, bs, free_order), P.Allocator(n, bs, free_order)
+
+
+def _same_state(o, p, seqs, bs):
+    assert o.num_free_blocks() == p.num_free_blocks()
+    for blk in range(o.num_blocks):
+        assert o.block_refcount(blk) == p.block_refcount(blk)
+    live = [s for s in seqs if s in o.tables]
+    for s in seqs:
+        assert p.context_len(s) == (o.lengths[s] if s in o.lengths else -1)
+    if live:
+        mb = max([len(o.tables[s]) for s in live] + [1])
+        to, co = o.build_block_tables(live, mb, pad=-7)
+        tp, cp = p.build_block_tables(live, mb, pad=-7)
+        assert np.array_equal(to, tp) and np.array_equal(co, cp)
+
+
+_ERR = {OAL.OutOfBlocks: "OUT_OF_BLOCKS", OAL.NotFound: "NOT_FOUND",
+        OAL.SharedWrite: "SHARED_WRITE", OAL.InvalidArg: "INVALID_ARG"}
+
+
+def _apply(o, p, op, x, y, k):
+    """Run one op on both allocators; results and errors must agree."""
+    res_o = res_p = None
+    err_o = err_p = None
+    try:
+        res_o = getattr(o, {"add": "add", "append": "append", "fork": "fork_prefix",
+                            "free": "free_seq"}[op])(*{"add": (x,), "append": (x, k),
+                                                       "fork": (x, y, k), "free": (x,)}[op])
+    except OAL.AllocatorError as e:
+        err_o = _ERR[type(e)]
+    try:
+        res_p = getattr(p, {"add": "add", "append": "append", "fork": "fork_prefix",
+                            "free": "free"}[op])(*{"add": (x,), "append": (x, k),
+                                                   "fork": (x, y, k), "free": (x,)}[op])
+    except P.PkvError as e:
+        err_p = e.code
+    assert err_o == err_p, (op, x, y, k, err_o, err_p)
+    if op == "append" and err_o is None:
+        assert list(res_o) == list(res_p)
+
+
+OPS = st.lists(st.tuples(st.sampled_from(["add", "append", "fork", "free"]),
+                         st.integers(0, 5), st.integers(0, 5), st.integers(0, 40)),
+               max_size=60)
+
+
+@settings(max_examples=300, deadline=None)
+@given(ops=OPS, bs=st.sampled_from([1, 4, 16, 32]), n=st.integers(0, 24), seed=st.integers(0, 9))
+def test_allocator_matches_oracle_random_ops(ops, bs, n, seed):
+    fo = W.permutation(seed, n) if n else None
+    o, p = _both(n, bs, fo)
+    for op in ops:
+        _apply(o, p, *op)
+        _same_state(o, p, range(6), bs)
+
+
+def test_allocator_matches_oracle_on_every_decode_shape():
+    """Full-size block tables, context lengths and new-token slots of the five
+    decode shapes, bit for bit."""
+    for i in range(5):
+        s = W.shape(i)
+        wl = W.make_workload(s, with_payload=False)
+        o, p = _both(wl.num_blocks, s.block_size, wl.free_order)
+        o.replay(wl.ops)
+        p.replay(wl.ops)
+        if s.new_tokens:
+            so = [o.append(b, 1)[0] for b in range(s.num_seqs)]
+            sp = p.append_tokens(list(range(s.num_seqs)), [1] * s.num_seqs)
+            assert list(so) == list(sp)
+        seqs = list(range(s.num_seqs))
+        mb = max(len(o.tables[b]) for b in seqs)
+        to, co = o.build_block_tables(seqs, mb)
+        tp, cp = p.build_block_tables(seqs, mb)
+        assert np.array_equal(to, tp) and np.array_equal(co, cp)
+        assert np.array_equal(co, wl.ctx)
+        assert p.num_free_blocks() == o.num_free_blocks()
+        if s.num_sharers:
+            pre = to[int(wl.sharers[0]), : s.shared_prefix_tokens // s.block_size]
+            assert all(p.block_refcount(int(b)) == s.num_sharers for b in pre)
+
+
+def test_batched_append_equals_sequential_and_is_all_or_nothing():
+    o, p = _both(40, 4, W.permutation(5, 40))
+    for s in range(3):
+        o.add(s)
+        p.add(s)
+    seqs, counts = [0, 1, 0, 2, 1], [3, 5, 2, 0, 9]
+    ref = []
+    for s, c in zip(seqs, counts):
+        ref += o.append(s, c)
+    got = p.append_tokens(seqs, counts)
+    assert list(got) == ref
+    _same_state(o, p, range(3), 4)
+    free = p.num_free_blocks()
+    with pytest.raises(P.PkvError) as e:
+        p.append_tokens([0, 1], [4, 4 * free + 1])
+    assert e.value.code == "OUT_OF_BLOCKS"
+    with pytest.raises(P.PkvError) as e:
+        p.append_tokens([0, 99], [1, 1])
+    assert e.value.code == "NOT_FOUND"
+    _same_state(o, p, range(3), 4)
+
+
+def test_allocator_errors_and_refcounts():
+    with pytest.raises(P.PkvError) as e:
+        P.Allocator(4, 16, free_order=[0, 1, 1, 3])
+    assert e.value.code == "INVALID_ARG"
+    a = P.Allocator(8, 4)
+    a.add(0)
+    a.append(0, 6)
+    a.add(1)
+    a.fork_prefix(0, 1, 6)  # full fork: shares the partly filled last block
+    blk = a.build_block_tables([0], 2)[0][0, 1]
+    assert a.block_refcount(int(blk)) == 2
+    with pytest.raises(P.PkvError) as e:
+        a.append(1, 1)
+    assert e.value.code == "SHARED_WRITE"
+    assert "shared" in str(e.value)
+    a.free(0)
+    assert a.block_refcount(int(blk)) == 1
+    a.append(1, 1)
+    with pytest.raises(P.PkvError) as e:
+        a.build_block_tables([1], 1)
+    assert e.value.code == "INVALID_ARG"
+    assert a.block_refcount(99) == -1 and a.context_len(42) == -1
+    a.free(1)
+    assert a.num_free_blocks() == 8
+
+
+# ------------------------------------------------------------------ argument checks
+def _decode(**kw):
+    args = dict(out=0, q=0, k=0, v=0, tables=0, max_blocks=4, ctx=0, max_ctx=64, B=2, Hq=4,
+                Hkv=4, D=128, bs=16, N=8, scale=0.1, part=0, ws=0, ws_bytes=0, dtype=P.BF16,
+                stream=None)
+    args.update(kw)
+    return P.lib.pkv_paged_attention_decode(
+        args["out"], args["q"], args["k"], args["v"], args["tables"], args["max_blocks"],
+        args["ctx"], args["max_ctx"], args["B"], args["Hq"], args["Hkv"], args["D"], args["bs"],
+        args["N"], args["scale"], args["part"], args["ws"], args["ws_bytes"], args["dtype"],
+        args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), -2), (dict(bs=8), -2), (dict(Hq=6, Hkv=4), -1), (dict(Hq=48, Hkv=1), -2),
+    (dict(dtype=7), -1), (dict(B=-1), -1), (dict(B=70000), -1), (dict(N=0), -1),
+    (dict(part=24), -1), (dict(part=-5), -1), (dict(max_ctx=-1), -1),
+    (dict(out=None, part=0), -1),
+])
+def test_decode_rejects_bad_arguments_before_launch(kw, code):
+    assert _decode(**kw) == code
+    assert P.lib.pkv_last_error().decode()
+
+
+def test_decode_workspace_and_partition_queries():
+    assert _decode(B=0) == 0  # nothing to do, nothing launched
+    assert P.decode_partition_size(32, 64, 8, 128, 16, 32768, P.PARTITION_AUTO) > 0
+    ps = P.decode_partition_size(32, 64, 8, 128, 16, 32768, 512)
+    assert ps == 512
+    need = P.decode_workspace_bytes(32, 64, 8, 128, 16, 32768, 512)
+    assert need == 32 * 64 * (32768 // 512) * (128 + 2) * 4
+    assert P.decode_workspace_bytes(4, 4, 4, 64, 16, 100, 0) == 0
+    # a partitioned call without workspace is refused before launch
+    assert _decode(part=16, q=1, k=1, v=1, tables=1, ctx=1, out=1) == -6
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=80), -2), (dict(T=-1), -1), (dict(kstride=100), -1), (dict(dtype=3), -1),
+])
+def test_cache_write_rejects_bad_arguments(kw, code):
+    a = dict(T=4, Hkv=2, D=64, bs=16, N=4, kstride=128, vstride=128, dtype=P.BF16)
+    a.update(kw)
+    st = P.lib.pkv_kv_reshape_and_cache(1, 1, 1, 1, 1, a["T"], a["Hkv"], a["D"], a["bs"], a["N"],
+                                        a["kstride"], a["vstride"], a["dtype"], None)
+    assert st == code
+
+
+def test_copy_blocks_rejects_bad_arguments():
+    assert P.lib.pkv_copy_blocks(1, 1, 1, -1, 4, 16, 2, 64, P.BF16, None) == -1
+    assert P.lib.pkv_copy_blocks(1, 1, 1, 0, 4, 16, 2, 64, P.BF16, None) == 0

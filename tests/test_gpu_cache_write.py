@@ -1,0 +1,81 @@
+"""GPU cache write and block copy, bit for bit against the oracle."""
+import numpy as np
+import pytest
+
+import oracle.allocator as OAL
+import oracle.cache_write as OC
+import workloads as W
+from gpu_cases import from_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+import paged_kv_cache_292_amd as P  # noqa: E402
+
+
+def _pool(dtype, N, bs, Hkv, D, seed):
+    n = N * bs * Hkv * D
+    if dtype == "f32":
+        return (W.normal_f32(seed, 1, n).reshape(N, bs, Hkv, D),
+                W.normal_f32(seed, 2, n).reshape(N, bs, Hkv, D))
+    return (W.normal_bf16_bits(seed, 1, n).reshape(N, bs, Hkv, D),
+            W.normal_bf16_bits(seed, 2, n).reshape(N, bs, Hkv, D))
+
+
+def test_decode_step_write_full_shape():
+    """128 new tokens of the LLaMA-13B-shaped step (40 kv heads of 128, bf16),
+    one per sequence, at the slots the allocator hands out."""
+    s = W.shape(2)
+    wl = W.make_workload(s)
+    a = P.Allocator(wl.num_blocks, s.block_size, wl.free_order)
+    a.replay(wl.ops)
+    slots = a.append_tokens(list(range(s.num_seqs)), [1] * s.num_seqs)
+    oa = OAL.BlockAllocator(wl.num_blocks, s.block_size, wl.free_order)
+    oa.replay(wl.ops)
+    assert np.array_equal(slots, [oa.append(b, 1)[0] for b in range(s.num_seqs)])
+    log(f"cache write {s.name}: {len(slots)} tokens")
+    kd, vd = to_dev(wl.k_cache, "bf16"), to_dev(wl.v_cache, "bf16")
+    P.kv_reshape_and_cache(to_dev(wl.new_k, "bf16"), to_dev(wl.new_v, "bf16"), kd, vd,
+                           torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    ko, vo = OC.reshape_and_cache(wl.new_k, wl.new_v, wl.k_cache, wl.v_cache, slots)
+    assert np.array_equal(from_dev(kd, "bf16"), ko)
+    assert np.array_equal(from_dev(vd, "bf16"), vo)
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+def test_write_padding_strides_and_out_of_range(dtype, D):
+    N, bs, Hkv, T = 9, 16, 3, 20
+    kc, vc = _pool(dtype, N, bs, Hkv, D, seed=5)
+    # key/value as slices of one fused [T, 3, Hkv, D] buffer (token stride 3*Hkv*D)
+    fused = (W.normal_f32(6, 3, T * 3 * Hkv * D).reshape(T, 3, Hkv, D) if dtype == "f32"
+             else W.normal_bf16_bits(6, 3, T * 3 * Hkv * D).reshape(T, 3, Hkv, D))
+    slots = W.permutation(8, N * bs)[:T].astype(np.int64)
+    slots[2] = -1
+    slots[7] = N * bs + 5  # outside the pool: skipped
+    fused_d = to_dev(fused, dtype)
+    kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
+    P.kv_reshape_and_cache(fused_d[:, 1], fused_d[:, 2], kd, vd, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    ok = slots.copy()
+    ok[7] = -1
+    ko, vo = OC.reshape_and_cache(fused[:, 1], fused[:, 2], kc, vc, ok)
+    assert np.array_equal(from_dev(kd, dtype), ko)
+    assert np.array_equal(from_dev(vd, dtype), vo)
+
+
+def test_copy_blocks():
+    N, bs, Hkv, D = 12, 32, 8, 128
+    kc, vc = _pool("bf16", N, bs, Hkv, D, seed=9)
+    pairs = np.array([[3, 7], [0, 11], [5, 2], [4, 99]], dtype=np.int64)  # last is skipped
+    kd, vd = to_dev(kc, "bf16"), to_dev(vc, "bf16")
+    P.copy_blocks(kd, vd, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    ke, ve = kc.copy(), vc.copy()
+    for s_, d_ in pairs[:3]:
+        ke[d_] = kc[s_]
+        ve[d_] = vc[s_]
+    assert np.array_equal(from_dev(kd, "bf16"), ke)
+    assert np.array_equal(from_dev(vd, "bf16"), ve)

@@ -1,0 +1,115 @@
+"""GPU parity of paged decode attention against the fp64 oracle.
+
+Every case builds its inputs from ``workloads``; tables and slots of the C++
+allocator are first checked bit for bit against the oracle allocator.
+Unused slots of each last block are NaN and table padding is garbage, so a
+kernel that reads outside a context fails.  Tolerances: fp32 1e-5 relative per
+(sequence, head) row; bf16 2e-2 max-abs plus a 1e-2 normwise self-check."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_cases import assert_close, build_step, log, oracle_full, oracle_rows, run_decode
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+import paged_kv_cache_292_amd as P  # noqa: E402  (fails loudly when the library is missing)
+
+# Scaled copies of the five decode shapes: same structure (group size, block
+# size, length mix, sharing), few enough sequences for a full oracle check.
+SMALL = {
+    0: W.shape(0),
+    1: W.scaled(W.shape(1), num_seqs=6),
+    2: W.scaled(W.shape(2), num_seqs=12),
+    3: W.scaled(W.shape(3), num_seqs=16, num_sharers=6),
+    4: W.scaled(W.shape(4), num_seqs=3),
+}
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("part", [0, P.PARTITION_AUTO, 512, 64])
+def test_small_shapes_full_output(cfg, part):
+    s = SMALL[cfg]
+    if part == 64 and s.block_size == 32:
+        part = 96
+    log(f"small shape {s.name} B={s.num_seqs} partition={part}")
+    st = build_step(s, poison=True, pad=2 ** 30)
+    got = run_decode(st, part)
+    ref = oracle_full(st)
+    assert_close(got, ref, s.dtype, f"{s.name} partition={part}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_full_shapes_sampled(cfg):
+    """Full-size shapes in the launch configuration the benchmark times
+    (automatic partitioning): sampled rows against the oracle, including the
+    longest and shortest sequences; every output finite."""
+    s = W.shape(cfg)
+    log(f"full shape {s.name} B={s.num_seqs}")
+    st = build_step(s, poison=True, pad=-1)
+    got = run_decode(st, P.PARTITION_AUTO)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(cfg)
+    bs_ = [int(np.argmax(st.ctx)), int(np.argmin(st.ctx))] + list(rng.integers(0, s.num_seqs, 6))
+    pairs = [(b, h) for b in bs_ for h in sorted(set([0, s.num_q_heads - 1,
+                                                      int(rng.integers(0, s.num_q_heads))]))]
+    ref = oracle_rows(st, pairs)
+    sub = np.stack([got[b, h] for b, h in pairs])
+    assert_close(sub, ref, s.dtype, f"{s.name} full, {len(pairs)} sampled rows")
+    if cfg in (2, 4):  # single pass must agree as well
+        got1 = run_decode(st, 0)
+        assert_close(np.stack([got1[b, h] for b, h in pairs]), ref, s.dtype,
+                     f"{s.name} full single pass")
+
+
+EDGE_CTX = (0, 1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1000, 1537)
+
+
+@pytest.mark.parametrize("dtype,D,bs,hq,hkv", [
+    ("f32", 64, 16, 4, 4), ("f32", 128, 32, 8, 2), ("bf16", 64, 32, 2, 1),
+    ("bf16", 128, 16, 8, 1), ("bf16", 128, 32, 16, 4), ("bf16", 128, 16, 4, 2),
+])
+@pytest.mark.parametrize("part", [0, 32, 512])
+def test_edge_lengths(dtype, D, bs, hq, hkv, part):
+    s = W.DecodeShape("edges", dtype, len(EDGE_CTX), hq, hkv, D, bs, "fixed",
+                      ctx_fixed=EDGE_CTX, seed=77)
+    log(f"edge lengths {dtype} D={D} bs={bs} G={hq // hkv} partition={part}")
+    st = build_step(s, poison=True, pad=-123456)
+    got = run_decode(st, part)
+    ref = oracle_full(st)
+    assert (got[0] == 0).all(), "empty context must give zeros"
+    assert_close(got, ref, dtype, f"edges {dtype} D{D} bs{bs} G{hq // hkv} p{part}")
+
+
+@pytest.mark.parametrize("cfg", [0, 2, 4])
+def test_peaked_softmax(cfg):
+    """q scaled by 8: the softmax is far from flat, so an indexing slip cannot
+    hide under averaging."""
+    s = {0: SMALL[0], 2: SMALL[2], 4: SMALL[4]}[cfg]
+    st = build_step(s, poison=True, q_scale=8.0)
+    for part in (0, P.PARTITION_AUTO):
+        assert_close(run_decode(st, part), oracle_full(st), s.dtype, f"{s.name} peaked p{part}")
+
+
+def test_placement_invariance_on_gpu():
+    """Two different physical placements of the same sequences give the same
+    output (within rounding)."""
+    s = SMALL[1]
+    a = build_step(s, poison=False)
+    b = build_step(dataclasses.replace(s, seed=s.seed), poison=False)
+    got_a = run_decode(a, 0)
+    # same payload, different free order: permute the pool on the host
+    perm = W.permutation(999, a.wl.num_blocks)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    b.k_cache[...] = a.k_cache[torch.from_numpy(inv).cuda()]
+    b.v_cache[...] = a.v_cache[torch.from_numpy(inv).cuda()]
+    tb = np.where(a.tables >= 0, perm[np.maximum(a.tables, 0)], -1).astype(np.int32)
+    b.tables_dev.copy_(torch.from_numpy(tb).cuda())
+    got_b = run_decode(b, 0)
+    np.testing.assert_array_equal(got_a, got_b)

@@ -40,6 +40,7 @@ __all__ = [
     "make_workload",
     "normal_f32",
     "f32_to_bf16_bits",
+    "normal_bf16_bits",
     "BF16_NAN_BITS",
 ]
 
@@ -139,6 +140,27 @@ def normal_f32(seed: int, stream: int, count: int) -> np.ndarray:
     return out
 
 
+def normal_bf16_bits(seed: int, stream: int, count: int) -> np.ndarray:
+    """The values of ``normal_f32(seed, stream, count)`` rounded to bf16 bits,
+    drawn and rounded chunk by chunk (no float32 copy of the whole array)."""
+    out = np.empty(count, dtype=np.uint16)
+    nchunks = (count + _CHUNK - 1) // _CHUNK
+
+    def fill(c: int) -> None:
+        lo = c * _CHUNK
+        hi = min(count, lo + _CHUNK)
+        out[lo:hi] = f32_to_bf16_bits(
+            _rng(seed, stream, c).standard_normal(hi - lo, dtype=np.float32))
+
+    if nchunks <= 1:
+        if count:
+            fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); returns the raw bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -152,8 +174,9 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def _payload(s: DecodeShape, stream: int, shp: Tuple[int, ...]) -> np.ndarray:
     n = int(np.prod(shp)) if shp else 1
-    x = normal_f32(s.seed, stream, n).reshape(shp)
-    return x if s.dtype == "f32" else f32_to_bf16_bits(x).reshape(shp)
+    if s.dtype == "f32":
+        return normal_f32(s.seed, stream, n).reshape(shp)
+    return normal_bf16_bits(s.seed, stream, n).reshape(shp)
 
 
 def context_lens(s: DecodeShape) -> np.ndarray:
