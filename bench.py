@@ -39,6 +39,9 @@ def _args():
     ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 single pass, else tokens")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profile", metavar="PREFIX", default=None,
+                    help="print a summary of rocprofv3 csv output PREFIX_kernel_{stats,trace}.csv "
+                         "(mean over the last --steps dispatches) and exit")
     return ap.parse_args()
 
 
@@ -56,25 +59,56 @@ def cpu_baseline(wl, tables, ctx, budget_s: float) -> dict:
     done_bytes = done_tok = 0
     nseq = 0
     t0 = time.perf_counter()
-    for b in order:
-        c = int(ctx[b])
-        OA.paged_decode(wl.q[b:b + 1], wl.k_cache, wl.v_cache, tables[b:b + 1], ctx[b:b + 1],
-                        s.scale, s.dtype)
-        done_bytes += c * 2 * s.num_kv_heads * s.head_dim * s.elem_bytes
-        done_tok += c
-        nseq += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    while time.perf_counter() - t0 < budget_s:  # whole passes over the batch order
+        for b in order:
+            c = int(ctx[b])
+            OA.paged_decode(wl.q[b:b + 1], wl.k_cache, wl.v_cache, tables[b:b + 1],
+                            ctx[b:b + 1], s.scale, s.dtype)
+            done_bytes += c * 2 * s.num_kv_heads * s.head_dim * s.elem_bytes
+            done_tok += c
+            nseq += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
     dt = time.perf_counter() - t0
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{nseq} of {s.num_seqs} sequences (all {s.num_q_heads} heads), "
-                      f"{done_tok} context tokens, {dt:.1f} s, numpy fp64",
+            "sample": f"{nseq} sequence decodes drawn from the {s.num_seqs}-sequence batch "
+                      f"(all {s.num_q_heads} heads each), {done_tok} context tokens, "
+                      f"{dt:.1f} s, numpy fp64",
             "seq_tokens_per_s": round(done_tok / dt, 1)}
+
+
+def summarize_profile(prefix: str, last: int) -> int:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run (csv output):
+    the stats table, and per kernel the mean over its last ``last`` dispatches
+    (the timed steps) from the trace."""
+    import csv
+    stats = list(csv.DictReader(open(prefix + "_kernel_stats.csv")))
+    trace = list(csv.DictReader(open(prefix + "_kernel_trace.csv")))
+    print("| kernel | calls | avg us | min us | max us | % time |")
+    print("|---|---|---|---|---|---|")
+    for r in stats:
+        print(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.2f} |")
+    print()
+    print(f"Mean over the last {last} dispatches of each kernel (the timed steps):")
+    print()
+    by = {}
+    for r in trace:
+        by.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    for name, v in by.items():
+        v.sort()
+        d = np.array([x[1] for x in v[-last:]]) / 1e3
+        print(f"- `{name[:110]}`: {d.mean():.2f} us (n={len(d)}, min {d.min():.2f}, max {d.max():.2f})")
+    return 0
 
 
 def main() -> int:
     args = _args()
+    if args.summarize_profile:
+        return summarize_profile(args.summarize_profile, args.steps)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         return 2

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIP_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
@@ -74,7 +74,8 @@ def build(verbose: bool = False) -> str:
             if line.strip():
                 print(line)
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5", *objs,
+          "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 
