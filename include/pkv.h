@@ -121,9 +121,13 @@ pkv_status pkv_kv_reshape_and_cache(const void* key, const void* value,
  * workspace     device scratch of at least pkv_decode_workspace_bytes(...)
  *               bytes when partitions are used (may be NULL otherwise).
  * Supported: head_dim in {64, 128}; block_size in {16, 32};
- *            num_q_heads a multiple of num_kv_heads with a group of at most
- *            16; partition_size a multiple of block_size (or 0 / -1);
- *            num_seqs <= 65535.
+ *            num_q_heads a multiple of num_kv_heads, the group
+ *            G = num_q_heads / num_kv_heads being 1..16 for bf16 and
+ *            1, 2, 4 or 8 for f32; partition_size a multiple of block_size
+ *            (or 0 / -1); num_seqs <= 65535.
+ * Kernels: a vector-ALU kernel for G = 1 (and f32), a matrix-core kernel
+ * (bf16 MFMA for q.K, fp32 MFMA for the weighted sum of V) for grouped
+ * query heads; see pkv_set_decode_path.
  * ---------------------------------------------------------------------- */
 #define PKV_PARTITION_AUTO (-1)
 
@@ -138,6 +142,18 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,
                                   int32_t block_size, int32_t max_context_len,
                                   int32_t partition_size, pkv_dtype dtype);
+
+/* Which decode kernel later calls use, process-wide (for tests and
+ * benchmarks): PKV_PATH_AUTO (default) picks the matrix-core kernel for bf16
+ * groups of 4..16 query heads and the vector kernel otherwise; PKV_PATH_VALU
+ * forces the vector kernel where it is built (G = 1, 2, 4, 8); PKV_PATH_MFMA
+ * forces the matrix-core kernel for every bf16 group of 2..16.  Not
+ * thread-safe against concurrent decode calls. */
+#define PKV_PATH_AUTO 0
+#define PKV_PATH_VALU 1
+#define PKV_PATH_MFMA 2
+pkv_status pkv_set_decode_path(int32_t path);
+int32_t pkv_get_decode_path(void);
 
 pkv_status pkv_paged_attention_decode(void* out, const void* q,
                                       const void* k_cache, const void* v_cache,

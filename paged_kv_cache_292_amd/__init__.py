@@ -4,7 +4,7 @@ Thin ctypes marshalling over the C ABI declared in ``include/pkv.h``; every
 step of the hot path runs in the library's HIP kernels or its C++ allocator.
 Device arguments are torch tensors (their ``data_ptr()``), launched on the
 current torch stream unless a stream is given.  The library must be built
-first (``python -m paged_kv_cache_292_amd.build``); importing this package
+first (``python paged_kv_cache_292_amd/build.py``); importing this package
 without it raises ``ImportError`` — there is no fallback.
 """
 from __future__ import annotations
@@ -18,14 +18,17 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "lib", "PkvError", "F32", "BF16", "PARTITION_AUTO",
     "kv_reshape_and_cache", "paged_attention_decode", "decode_workspace_bytes",
-    "decode_partition_size", "copy_blocks", "Allocator", "EXPORTS", "version",
+    "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path",
+    "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 F32 = 0
 BF16 = 1
 PARTITION_AUTO = -1
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 
 STATUS = {
     0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "OUT_OF_BLOCKS", -4: "NOT_FOUND",
@@ -45,6 +48,8 @@ EXPORTS = {
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
                                           _vp]),
+    "pkv_set_decode_path": (_i32, [_i32]),
+    "pkv_get_decode_path": (_i32, []),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_allocator_create": (_i32, [_i32, _i32, _P(_i32), _P(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
@@ -68,7 +73,7 @@ def _load():
 
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m paged_kv_cache_292_amd.build`")
+                          "`python paged_kv_cache_292_amd/build.py`")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in EXPORTS.items():
         fn = getattr(handle, name)
@@ -154,6 +159,15 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
         int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
         ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode")
+
+
+def set_decode_path(path: int) -> None:
+    """Process-wide decode kernel choice: PATH_AUTO, PATH_VALU or PATH_MFMA."""
+    _check(lib.pkv_set_decode_path(int(path)), "set_decode_path")
+
+
+def get_decode_path() -> int:
+    return int(lib.pkv_get_decode_path())
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:

@@ -1,6 +1,7 @@
 """Build libpkv.so in-tree: HIP kernels for gfx950 plus the host allocator.
 
-Usage: ``python -m paged_kv_cache_292_amd.build`` (or ``build()`` from Python).
+Usage: ``python paged_kv_cache_292_amd/build.py`` (run as a file: importing the
+package would load the library being rebuilt).
 Host-only C++ is compiled with g++; ``.hip`` files with hipcc for gfx950;
 everything is linked by hipcc into ``paged_kv_cache_292_amd/libpkv.so``.
 """

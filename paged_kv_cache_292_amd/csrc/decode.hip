@@ -282,6 +282,231 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Partition kernel for grouped query heads (2..16 q heads per kv head, bf16)
+// on the matrix cores.
+//
+// Per 16-token chunk and kv head:
+//   S^T[16 tokens x 16 heads] = K[16 x D] . Q^T[D x 16]   (bf16 MFMA 16x16x32,
+//     K rows as operand A, the group's q heads as operand B, padded to 16)
+//   O^T[D x 16 heads] += V^T[D x 16 tokens] . P^T[16 x 16] (fp32 MFMA 16x16x4,
+//     four calls of 4 tokens per 16 output dims; V needs no transpose because
+//     each lane feeds one element per call, and P stays in fp32)
+// Lane l (c = l / 16, n = l % 16) holds the scores of head n for tokens
+// 4c..4c+3 and accumulates head n's output for dims [D/4 * c, D/4 * (c+1)),
+// so the online-softmax state of a head lives in its own lanes.  The dot
+// product's k order is permuted identically in both operands (lane group c,
+// step j covers dims 8c + 32j .. +7), which leaves the sum unchanged.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+template <int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int KSTEPS = D / 32;  // QK^T MFMA steps over head_dim
+  constexpr int EPL = D / 16;     // V elements per lane (one 16- or 8-byte load)
+  constexpr int VW = EPL / 2;     // 32-bit words per V load
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane >> 4;
+  const int n = lane & 15;
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+
+  const int ctx = clamp_ctx(a, b);
+  const int t0 = part * a.partition;
+  const int t1 = min(ctx, t0 + a.partition);
+  const int nparts = (ctx + a.partition - 1) / a.partition;
+  if (t0 >= t1) {
+    if (ctx == 0 && part == 0) {
+      for (int i = threadIdx.x; i < G * D; i += NW * 64)
+        store_elem<uint16_t>(a.out, (size_t(b) * Hq + kvh * G) * D + i, 0.0f);
+    }
+    return;
+  }
+
+  // Q^T operand: head n of the group (zeros past G), dims 8c + 32j .. +7.
+  uint4 qop[KSTEPS];
+  {
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                         (size_t(b) * Hq + size_t(kvh) * G + (n < G ? n : 0)) * D + 8 * c;
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+      uint4 v = *reinterpret_cast<const uint4*>(qh + 32 * j);
+      qop[j] = n < G ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  f32x4_t acc[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -FLT_MAX, l = 0.0f;
+
+  const int row_stride = Hkv * D;
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+  const int c_begin = t0 / kChunk;
+  const int c_end = (t1 + kChunk - 1) / kChunk;
+
+  // Byte offsets inside a chunk: K row of token n (dims 8c + 32j), V row of
+  // token 4c + i (dims EPL*n ..).  Masked slots fall back to the chunk's row 0.
+  uint32_t koff[KSTEPS], kmask[KSTEPS], voff[4], vmask[4];
+#pragma unroll
+  for (int j = 0; j < KSTEPS; ++j) {
+    kmask[j] = uint32_t((8 * c + 32 * j) * 2);
+    koff[j] = uint32_t((n * row_stride + 8 * c + 32 * j) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    vmask[i] = uint32_t(EPL * n * 2);
+    voff[i] = uint32_t(((4 * c + i) * row_stride + EPL * n) * 2);
+  }
+
+  struct Regs {
+    uint4 k[KSTEPS];
+    uint32_t v[4][VW];
+  };
+  auto load_chunk = [&](int ch, Regs& r) {
+    const int tc = __builtin_amdgcn_readfirstlane(ch * kChunk);
+    int bid = scalar_read(tbl + tc / BS);
+    bid = (unsigned)bid < (unsigned)a.num_blocks ? bid : 0;
+    const size_t rowbase = ((size_t(bid) * BS + (tc % BS)) * row_stride + size_t(kvh) * D) * 2;
+    const char* kb = kc + rowbase;
+    const char* vb = vc + rowbase;
+    const bool kvalid = tc + n < t1;
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j)
+      r.k[j] = *reinterpret_cast<const uint4*>(kb + (kvalid ? koff[j] : kmask[j]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = tc + 4 * c + i < t1 ? voff[i] : vmask[i];
+      if constexpr (VW == 4) {
+        uint4 x = *reinterpret_cast<const uint4*>(vb + off);
+        r.v[i][0] = x.x;
+        r.v[i][1] = x.y;
+        r.v[i][2] = x.z;
+        r.v[i][3] = x.w;
+      } else {
+        uint2 x = *reinterpret_cast<const uint2*>(vb + off);
+        r.v[i][0] = x.x;
+        r.v[i][1] = x.y;
+      }
+    }
+  };
+
+  auto consume = [&](int ch, const Regs& r) {
+    const int tc = ch * kChunk;
+    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
+                                                  __builtin_bit_cast(bf16x8_t, qop[j]), s, 0, 0,
+                                                  0);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = tc + 4 * c + i < t1 ? s[i] * a.scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(p[i] - mn);
+    float ps = (p[0] + p[1]) + (p[2] + p[3]);
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const uint32_t w = r.v[i][j >> 1];
+        const float v = (j & 1) ? bf16_hi(w) : bf16_lo(w);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[i], acc[j], 0, 0, 0);
+      }
+    }
+  };
+
+  Regs ra, rb;
+  int ch = c_begin + wave;
+  if (ch < c_end) {
+    load_chunk(ch, ra);
+    while (true) {
+      int cn = ch + NW < c_end ? ch + NW : ch;
+      load_chunk(cn, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(ch, ra);
+      ch += NW;
+      if (ch >= c_end) break;
+      cn = ch + NW < c_end ? ch + NW : ch;
+      load_chunk(cn, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(ch, rb);
+      ch += NW;
+      if (ch >= c_end) break;
+    }
+  }
+
+  // acc[j][r] = O[head n][EPL*(4c + r) + j] (unnormalised, this wave's tokens).
+  const bool single = nparts == 1;
+  const size_t head0 = size_t(b) * Hq + size_t(kvh) * G;
+  auto finish = [&](int h, int d, float o, float mm, float ll) {
+    if (single) {
+      store_elem<uint16_t>(a.out, (head0 + h) * D + d, o / ll);
+    } else {
+      const size_t pi = (head0 + h) * a.max_parts + part;
+      a.part_o[pi * D + d] = o / ll;
+      if (d == 0) {
+        a.part_ml[2 * pi] = mm;
+        a.part_ml[2 * pi + 1] = ll;
+      }
+    }
+  };
+  if constexpr (NW == 1) {
+    if (n < G) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) finish(n, EPL * (4 * c + r) + j, acc[j][r], m, l);
+    }
+  } else {
+    __shared__ float s_o[NW][16][D];
+    __shared__ float s_ml[NW][16][2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) s_o[wave][n][EPL * (4 * c + r) + j] = acc[j][r];
+    if (c == 0) {
+      s_ml[wave][n][0] = m;
+      s_ml[wave][n][1] = l;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += NW * 64) {
+      const int h = i / D;
+      const int d = i % D;
+      float M = s_ml[0][h][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+      float L = 0.0f, O = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = fast_exp2(s_ml[w][h][0] - M);
+        L = fmaf(s_ml[w][h][1], f, L);
+        O = fmaf(s_o[w][h][d], f, O);
+      }
+      finish(h, d, O, M, L);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Log-sum-exp merge of the partitions of one (sequence, query head).
 // out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - max_p m_p).
 template <typename T, int D>
@@ -320,7 +545,13 @@ __global__ __launch_bounds__(64) void reduce_partitions_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Host side.
 
-constexpr int kNW = 4;
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+#ifndef PKV_AUTO_PARTITION
+#define PKV_AUTO_PARTITION 512
+#endif
+constexpr int kNW = PKV_DECODE_WAVES;  // waves per workgroup
 
 template <typename T, int D, int BS, int G>
 hipError_t launch_valu(const DecodeArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
@@ -329,9 +560,32 @@ hipError_t launch_valu(const DecodeArgs& a, int num_seqs, hipStream_t st, int gr
   return hipGetLastError();
 }
 
+template <int D, int BS>
+hipError_t launch_mfma(const DecodeArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
+  dim3 grid(grid_parts, a.num_kv_heads, num_seqs);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW>), grid, dim3(kNW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+// Process-wide kernel choice (tests and benchmarks compare the two paths).
+int g_decode_path = PKV_PATH_AUTO;
+
+// Matrix cores for bf16 groups of 4..16 query heads per kv head (and for the
+// group sizes the vector kernel is not built for); vector ALUs otherwise.
+bool use_mfma(bool bf16, int G) {
+  if (!bf16 || G < 2) return false;
+  const bool valu_ok = G == 2 || G == 4 || G == 8;
+  if (g_decode_path == PKV_PATH_VALU && valu_ok) return false;
+  if (g_decode_path == PKV_PATH_MFMA) return true;
+  return G >= 4 || !valu_ok;
+}
+
 template <typename T, int D, int BS>
 hipError_t dispatch_group(const DecodeArgs& a, int G, int num_seqs, hipStream_t st,
                           int grid_parts) {
+  if constexpr (sizeof(T) == 2) {
+    if (use_mfma(true, G)) return launch_mfma<D, BS>(a, num_seqs, st, grid_parts);
+  }
   switch (G) {
     case 1: return launch_valu<T, D, BS, 1>(a, num_seqs, st, grid_parts);
     case 2: return launch_valu<T, D, BS, 2>(a, num_seqs, st, grid_parts);
@@ -355,12 +609,16 @@ hipError_t launch_reduce(const DecodeArgs& a, int num_seqs, hipStream_t st) {
   return hipGetLastError();
 }
 
-bool group_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+bool group_supported(bool bf16, int g) {
+  if (g == 1 || g == 2 || g == 4 || g == 8) return true;
+  return bf16 && g >= 2 && g <= 16;
+}
 
 // Partition length actually used, 0 = single pass.  AUTO splits long
 // contexts into 512-token partitions.
 int32_t resolve_partition(int32_t max_context_len, int32_t partition_size) {
-  if (partition_size == PKV_PARTITION_AUTO) return max_context_len > 1024 ? 512 : 0;
+  if (partition_size == PKV_PARTITION_AUTO)
+    return max_context_len > 2 * PKV_AUTO_PARTITION ? PKV_AUTO_PARTITION : 0;
   return partition_size;
 }
 
@@ -376,6 +634,15 @@ size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
 }  // namespace pkv
 
 using pkv::fail;
+
+extern "C" pkv_status pkv_set_decode_path(int32_t path) {
+  if (path != PKV_PATH_AUTO && path != PKV_PATH_VALU && path != PKV_PATH_MFMA)
+    return fail(PKV_ERR_INVALID_ARG, "set_decode_path: unknown path %d", path);
+  pkv::g_decode_path = path;
+  return pkv::ok();
+}
+
+extern "C" int32_t pkv_get_decode_path(void) { return pkv::g_decode_path; }
 
 extern "C" int32_t pkv_decode_partition_size(int32_t, int32_t, int32_t, int32_t, int32_t,
                                              int32_t max_context_len, int32_t partition_size,
@@ -418,9 +685,10 @@ extern "C" pkv_status pkv_paged_attention_decode(
   if (block_size != 16 && block_size != 32)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: block_size=%d (16 or 32)",
                 block_size);
-  if (!pkv::group_supported(G))
+  if (!pkv::group_supported(dtype == PKV_BF16, G))
     return fail(PKV_ERR_UNSUPPORTED,
-                "paged_attention_decode: query heads per kv head = %d (1, 2, 4 or 8)", G);
+                "paged_attention_decode: query heads per kv head = %d (1..16 for bf16; "
+                "1, 2, 4 or 8 for f32)", G);
   if (num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
       max_context_len > (1 << 29))
     return fail(PKV_ERR_INVALID_ARG,

@@ -67,6 +67,37 @@ def test_full_shapes_sampled(cfg):
                      f"{s.name} full single pass")
 
 
+@pytest.fixture
+def decode_path():
+    """Select a decode kernel for one test, restore the automatic choice after."""
+    yield P.set_decode_path
+    P.set_decode_path(P.PATH_AUTO)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("path", [P.PATH_VALU, P.PATH_MFMA])
+@pytest.mark.parametrize("part", [0, P.PARTITION_AUTO])
+def test_grouped_query_both_kernels(cfg, path, part, decode_path):
+    """The vector and matrix-core kernels on the grouped-query shapes."""
+    decode_path(path)
+    s = SMALL[cfg]
+    log(f"{s.name} path={path} partition={part}")
+    st = build_step(s, poison=True, pad=7 * 10 ** 8)
+    assert_close(run_decode(st, part), oracle_full(st), s.dtype, f"{s.name} path{path} p{part}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (10, 2), (12, 2), (32, 2), (16, 1), (14, 7)])
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 32)])
+def test_matrix_core_group_sizes(hq, hkv, D, bs):
+    """Group sizes 3, 5, 6, 16, 16, 2 (bf16): only the matrix-core kernel
+    covers the odd ones."""
+    s = W.DecodeShape("groups", "bf16", 5, hq, hkv, D, bs, "fixed",
+                      ctx_fixed=(1, 40, 333, 1024, 2049), seed=hq * 100 + hkv)
+    st = build_step(s, poison=True, pad=-1)
+    for part in (0, 64):
+        assert_close(run_decode(st, part), oracle_full(st), "bf16", f"G{hq // hkv} D{D} bs{bs} p{part}")
+
+
 EDGE_CTX = (0, 1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1000, 1537)
 
 
@@ -75,15 +106,18 @@ EDGE_CTX = (0, 1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1000, 1537)
     ("bf16", 128, 16, 8, 1), ("bf16", 128, 32, 16, 4), ("bf16", 128, 16, 4, 2),
 ])
 @pytest.mark.parametrize("part", [0, 32, 512])
-def test_edge_lengths(dtype, D, bs, hq, hkv, part):
+def test_edge_lengths(dtype, D, bs, hq, hkv, part, decode_path):
     s = W.DecodeShape("edges", dtype, len(EDGE_CTX), hq, hkv, D, bs, "fixed",
                       ctx_fixed=EDGE_CTX, seed=77)
-    log(f"edge lengths {dtype} D={D} bs={bs} G={hq // hkv} partition={part}")
     st = build_step(s, poison=True, pad=-123456)
-    got = run_decode(st, part)
     ref = oracle_full(st)
-    assert (got[0] == 0).all(), "empty context must give zeros"
-    assert_close(got, ref, dtype, f"edges {dtype} D{D} bs{bs} G{hq // hkv} p{part}")
+    paths = [P.PATH_VALU, P.PATH_MFMA] if dtype == "bf16" and hq > hkv else [P.PATH_AUTO]
+    for path in paths:
+        decode_path(path)
+        log(f"edge lengths {dtype} D={D} bs={bs} G={hq // hkv} partition={part} path={path}")
+        got = run_decode(st, part)
+        assert (got[0] == 0).all(), "empty context must give zeros"
+        assert_close(got, ref, dtype, f"edges {dtype} D{D} bs{bs} G{hq // hkv} p{part} path{path}")
 
 
 @pytest.mark.parametrize("cfg", [0, 2, 4])
