@@ -247,20 +247,29 @@ def main() -> int:
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     part_used = P.decode_partition_size(B, Hq, Hkv, D, bs, max_ctx_final, args.partition, dt_code)
 
-    # pinned host staging, double-buffered; device tables/ctx/slots
+    # One pinned staging buffer per in-flight step, laid out as the device
+    # buffer it is copied to: slots int64 [B] | tables int32 [B, max_blocks] |
+    # context lengths int32 [B].  One H2D copy per step.
     nbuf = 2
-    h_tables = [torch.empty((B, max_blocks), dtype=torch.int32).pin_memory() for _ in range(nbuf)]
-    h_ctx = [torch.empty(B, dtype=torch.int32).pin_memory() for _ in range(nbuf)]
-    h_slots = [torch.empty(max(B, 1), dtype=torch.int64).pin_memory() for _ in range(nbuf)]
-    d_tables = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
-    d_ctx = torch.empty(B, dtype=torch.int32, device=dev)
-    d_slots = torch.empty(max(B, 1), dtype=torch.int64, device=dev)
-    ones = np.ones(B, dtype=np.int32)
-    copied = [None] * nbuf
+    n_slot_b, n_tab_b, n_ctx_b = 8 * B, 4 * B * max_blocks, 4 * B
+    stage_bytes = n_slot_b + n_tab_b + n_ctx_b
+    h_stage = [torch.empty(stage_bytes, dtype=torch.uint8).pin_memory() for _ in range(nbuf)]
+    h_views = []
+    for hs in h_stage:
+        a_ = hs.numpy()
+        h_views.append((a_[:n_slot_b].view(np.int64),
+                        a_[n_slot_b:n_slot_b + n_tab_b].view(np.int32).reshape(B, max_blocks),
+                        a_[n_slot_b + n_tab_b:].view(np.int32)))
+    d_stage = torch.empty(stage_bytes, dtype=torch.uint8, device=dev)
+    d_slots = d_stage[:n_slot_b].view(torch.int64)
+    d_tables = d_stage[n_slot_b:n_slot_b + n_tab_b].view(torch.int32).view(B, max_blocks)
+    d_ctx = d_stage[n_slot_b + n_tab_b:].view(torch.int32)
+    copied = [torch.cuda.Event() for _ in range(nbuf)]
     stream = torch.cuda.current_stream()
+    new_k_steps = [new_k[i] for i in range(total_steps)] if step_new else None
+    new_v_steps = [new_v[i] for i in range(total_steps)] if step_new else None
 
     # per-step algorithmic bytes of the decode call
-    G = Hq // Hkv
     E = s.elem_bytes
 
     def decode_bytes(ctx):
@@ -275,38 +284,30 @@ def main() -> int:
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(total_steps)]
-    kv_bytes = []
-    alg_bytes = []
-    ctx_tokens = []
+    ctx_hist = []
+    host_s = []
 
     def step(i):
+        t_h = time.perf_counter()
         j = i % nbuf
-        if copied[j] is not None:
+        if i >= nbuf:
             copied[j].synchronize()  # staging buffer j is free again
-        tb = h_tables[j].numpy()
-        cx = h_ctx[j].numpy()
-        sl = h_slots[j].numpy()
+        sl, tb, cx = h_views[j]
         if step_new:
-            alloc.append_tokens(seqs, ones, out=sl)
-        alloc.build_block_tables(seqs, max_blocks, pad=-1, tables_out=tb, ctx_out=cx)
-        maxc = int(cx.max())
-        d_tables.copy_(h_tables[j], non_blocking=True)
-        d_ctx.copy_(h_ctx[j], non_blocking=True)
+            maxc = alloc.decode_step_prepare(seqs, max_blocks, sl, tb, cx)
+        else:
+            alloc.build_block_tables(seqs, max_blocks, pad=-1, tables_out=tb, ctx_out=cx)
+            maxc = int(cx.max())
+        d_stage.copy_(h_stage[j], non_blocking=True)
+        copied[j].record(stream)
         if step_new:
-            d_slots.copy_(h_slots[j], non_blocking=True)
-        e = torch.cuda.Event()
-        e.record(stream)
-        copied[j] = e
-        if step_new:
-            P.kv_reshape_and_cache(new_k[i], new_v[i], k_cache, v_cache, d_slots[:B])
+            P.kv_reshape_and_cache(new_k_steps[i], new_v_steps[i], k_cache, v_cache, d_slots)
         ev[i][0].record(stream)
         P.paged_attention_decode(out, q, k_cache, v_cache, d_tables, d_ctx, maxc, s.scale,
                                  args.partition, workspace)
         ev[i][1].record(stream)
-        kvb, algb = decode_bytes(cx.astype(np.int64))
-        kv_bytes.append(kvb)
-        alg_bytes.append(algb)
-        ctx_tokens.append(int(cx.sum()))
+        ctx_hist.append(cx.copy())
+        host_s.append(time.perf_counter() - t_h)
 
     for i in range(args.warmup):
         step(i)
@@ -318,6 +319,10 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     K = args.steps
     timed = slice(args.warmup, total_steps)
+    per_step = [decode_bytes(c.astype(np.int64)) for c in ctx_hist]
+    kv_bytes = [x[0] for x in per_step]
+    alg_bytes = [x[1] for x in per_step]
+    ctx_tokens = [int(c.sum()) for c in ctx_hist]
     kv_t = sum(kv_bytes[timed])
     tok_t = sum(ctx_tokens[timed])
     dec_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total_steps)])
@@ -342,6 +347,7 @@ def main() -> int:
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(tok_t / elapsed, 1),
         "decode_tokens_per_s": round(B * K / elapsed, 1),
+        "host_us_per_step": round(float(np.mean(host_s[timed])) * 1e6, 1),
         "config": {
             "workload": s.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": bs, "mean_context": round(tok_t / K / B, 1),

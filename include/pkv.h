@@ -236,6 +236,21 @@ pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64_t* seq_ids
                                   int32_t pad_value, int32_t* tables_out,
                                   int32_t* context_lens_out);
 
+/* One decode step's host work in one call: every sequence in seq_ids grows
+ * by one token (slots_out, host int64 [num_seqs], receives the new slots in
+ * order), then tables_out (host int32 [num_seqs, max_blocks_per_seq]) and
+ * context_lens_out (host int32 [num_seqs]) receive the grown tables and
+ * lengths, and *max_context_len_out their maximum (either may be NULL).
+ * seq_ids must be distinct.  All-or-nothing: PKV_ERR_NOT_FOUND,
+ * PKV_ERR_INVALID_ARG (a repeated id, or a table that would not fit),
+ * PKV_ERR_OUT_OF_BLOCKS or PKV_ERR_SHARED_WRITE leave the allocator
+ * unchanged. */
+pkv_status pkv_decode_step_prepare(pkv_allocator* a, const int64_t* seq_ids,
+                                   int32_t num_seqs, int32_t max_blocks_per_seq,
+                                   int32_t pad_value, int64_t* slots_out,
+                                   int32_t* tables_out, int32_t* context_lens_out,
+                                   int32_t* max_context_len_out);
+
 int32_t pkv_num_free_blocks(const pkv_allocator* a);
 /* Reference count of a block (0 = free), -1 for an id outside the pool. */
 int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block_id);

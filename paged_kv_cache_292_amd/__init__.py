@@ -59,6 +59,8 @@ EXPORTS = {
     "pkv_append_tokens": (_i32, [_vp, _P(_i64), _P(_i32), _i32, _P(_i64)]),
     "pkv_seq_free": (_i32, [_vp, _i64]),
     "pkv_build_block_tables": (_i32, [_vp, _P(_i64), _i32, _i32, _i32, _P(_i32), _P(_i32)]),
+    "pkv_decode_step_prepare": (_i32, [_vp, _P(_i64), _i32, _i32, _i32, _P(_i64), _P(_i32),
+                                       _P(_i32), _P(_i32)]),
     "pkv_num_free_blocks": (_i32, [_vp]),
     "pkv_block_refcount": (_i32, [_vp, _i32]),
     "pkv_seq_context_len": (_i64, [_vp, _i64]),
@@ -249,6 +251,20 @@ class Allocator:
                                           c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
                "build_block_tables")
         return t, c
+
+    def decode_step_prepare(self, seqs: np.ndarray, max_blocks: int, slots_out: np.ndarray,
+                            tables_out: np.ndarray, ctx_out: np.ndarray, pad: int = -1) -> int:
+        """Grow every sequence in ``seqs`` (int64) by one token and write the
+        new slots, the tables and context lengths into the given host arrays
+        (contiguous int64 / int32 / int32); returns the longest context."""
+        mx = ctypes.c_int32(0)
+        _check(lib.pkv_decode_step_prepare(
+            self._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(seqs), max_blocks,
+            pad, slots_out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            tables_out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            ctx_out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(mx)),
+            "decode_step_prepare")
+        return int(mx.value)
 
     def num_free_blocks(self) -> int:
         return int(lib.pkv_num_free_blocks(self._h))

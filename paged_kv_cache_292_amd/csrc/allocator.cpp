@@ -15,6 +15,7 @@
 #include <deque>
 #include <new>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -219,4 +220,43 @@ extern "C" int32_t pkv_seq_num_blocks(const pkv_allocator* a, int64_t seq_id) {
   if (!a) return -1;
   auto it = a->seqs.find(seq_id);
   return it == a->seqs.end() ? -1 : int32_t(it->second.blocks.size());
+}
+
+extern "C" pkv_status pkv_decode_step_prepare(pkv_allocator* a, const int64_t* seq_ids,
+                                              int32_t num_seqs, int32_t max_blocks_per_seq,
+                                              int32_t pad_value, int64_t* slots_out,
+                                              int32_t* tables_out, int32_t* context_lens_out,
+                                              int32_t* max_context_len_out) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "decode_step_prepare: NULL allocator");
+  if (num_seqs < 0 || (num_seqs > 0 && (!seq_ids || !slots_out || !tables_out)))
+    return fail(PKV_ERR_INVALID_ARG, "decode_step_prepare: bad arguments");
+  // every sequence must exist, appear once and fit its grown table before
+  // anything changes
+  std::unordered_set<int64_t> seen;
+  seen.reserve(size_t(num_seqs) * 2);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (!seen.insert(seq_ids[i]).second)
+      return fail(PKV_ERR_INVALID_ARG, "decode_step_prepare: sequence %lld listed twice",
+                  (long long)seq_ids[i]);
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PKV_ERR_NOT_FOUND, "decode_step_prepare: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+    if (a->blocks_for(it->second.len + 1) > max_blocks_per_seq)
+      return fail(PKV_ERR_INVALID_ARG,
+                  "decode_step_prepare: sequence %lld would need more than %d blocks",
+                  (long long)seq_ids[i], max_blocks_per_seq);
+  }
+  static thread_local std::vector<int32_t> ones;
+  if (int32_t(ones.size()) < num_seqs) ones.assign(size_t(num_seqs), 1);
+  pkv_status st = pkv_append_tokens(a, seq_ids, ones.data(), num_seqs, slots_out);
+  if (st != PKV_OK) return st;
+  st = pkv_build_block_tables(a, seq_ids, num_seqs, max_blocks_per_seq, pad_value, tables_out,
+                              context_lens_out);
+  if (st != PKV_OK) return st;  // cannot happen: checked above
+  int32_t mx = 0;
+  if (context_lens_out)
+    for (int32_t i = 0; i < num_seqs; ++i) mx = context_lens_out[i] > mx ? context_lens_out[i] : mx;
+  if (max_context_len_out) *max_context_len_out = mx;
+  return pkv::ok();
 }

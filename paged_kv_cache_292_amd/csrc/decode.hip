@@ -282,27 +282,47 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Partition kernel for grouped query heads (2..16 q heads per kv head, bf16)
-// on the matrix cores.
+// Partition kernel on the matrix cores (bf16, 1..16 q heads per kv head).
 //
-// Per 16-token chunk and kv head:
-//   S^T[16 tokens x 16 heads] = K[16 x D] . Q^T[D x 16]   (bf16 MFMA 16x16x32,
-//     K rows as operand A, the group's q heads as operand B, padded to 16)
-//   O^T[D x 16 heads] += V^T[D x 16 tokens] . P^T[16 x 16] (fp32 MFMA 16x16x4,
-//     four calls of 4 tokens per 16 output dims; V needs no transpose because
-//     each lane feeds one element per call, and P stays in fp32)
-// Lane l (c = l / 16, n = l % 16) holds the scores of head n for tokens
-// 4c..4c+3 and accumulates head n's output for dims [D/4 * c, D/4 * (c+1)),
-// so the online-softmax state of a head lives in its own lanes.  The dot
-// product's k order is permuted identically in both operands (lane group c,
-// step j covers dims 8c + 32j .. +7), which leaves the sum unchanged.
+// Per 16-token chunk and kv head, with the group's q heads padded to 16:
+//   S^T[16 tokens x 16 heads] = K[16 x D] . Q^T[D x 16]    bf16 MFMA 16x16x32
+//     (K rows as operand A, q heads as operand B, D/32 steps)
+//   O^T[D x 16 heads] += V^T[D x 16 tokens] . P^T[16 x 16] bf16 MFMA 16x16x16
+//     (D/16 calls, one per group of 16 output dims)
+// Lane l (c = l / 16, n = l % 16) gets the scores of head n for tokens
+// 4c..4c+3, exactly the four k entries of P^T it must supply, and it has
+// loaded V rows 4c..4c+3 at dims EPL*n .. EPL*n+EPL-1, whose element t of
+// each row forms its V^T operand for output tile t (dims EPL*m + t).  So no
+// data crosses lanes between the two products: only half-words are packed.
+// Lane l accumulates head n's output at dims EPL*(4c + r) + t (r < 4, t <
+// EPL), i.e. the contiguous range [4*EPL*c, 4*EPL*(c+1)).
+//
+// Online softmax with a lazy maximum: a head's reference max m only moves
+// when a chunk's score exceeds it by more than 2^8 (in base-2 units), so
+// p = 2^(s - m) <= 256 and the accumulator is rescaled only in those rare
+// chunks (a wave-uniform branch).  The final division by the sum makes the
+// result independent of the reference chosen.  P is rounded to bf16 for the
+// second product; sums and accumulators stay fp32.
+// The q.K^T k order is permuted identically in both operands (lane group c,
+// step j covers dims 8c + 32j .. +7), which leaves the dot product unchanged.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLazyMax = 8.0f;  // log2 of the largest p allowed before rescaling
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2v_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));  // RNE
+}
 
 template <int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int KSTEPS = D / 32;  // QK^T MFMA steps over head_dim
-  constexpr int EPL = D / 16;     // V elements per lane (one 16- or 8-byte load)
+  constexpr int KSTEPS = D / 32;  // q.K^T MFMA steps over head_dim
+  constexpr int EPL = D / 16;     // V elements per lane per token row = PV tiles
   constexpr int VW = EPL / 2;     // 32-bit words per V load
 
   const int lane = threadIdx.x & 63;
@@ -335,15 +355,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                          (size_t(b) * Hq + size_t(kvh) * G + (n < G ? n : 0)) * D + 8 * c;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
-      uint4 v = *reinterpret_cast<const uint4*>(qh + 32 * j);
+      const uint4 v = *reinterpret_cast<const uint4*>(qh + 32 * j);
       qop[j] = n < G ? v : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 
   f32x4_t acc[EPL];
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -FLT_MAX, l = 0.0f;
+  for (int t = 0; t < EPL; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -FLT_MAX;  // reference max of head n (same in its four lanes)
+  float l = 0.0f;      // this lane's share of head n's sum
 
   const int row_stride = Hkv * D;
   const char* kc = static_cast<const char*>(a.k_cache);
@@ -354,17 +375,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 
   // Byte offsets inside a chunk: K row of token n (dims 8c + 32j), V row of
   // token 4c + i (dims EPL*n ..).  Masked slots fall back to the chunk's row 0.
-  uint32_t koff[KSTEPS], kmask[KSTEPS], voff[4], vmask[4];
+  uint32_t koff[KSTEPS], kmask[KSTEPS], voff[4];
 #pragma unroll
   for (int j = 0; j < KSTEPS; ++j) {
     kmask[j] = uint32_t((8 * c + 32 * j) * 2);
     koff[j] = uint32_t((n * row_stride + 8 * c + 32 * j) * 2);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    vmask[i] = uint32_t(EPL * n * 2);
-    voff[i] = uint32_t(((4 * c + i) * row_stride + EPL * n) * 2);
-  }
+  for (int i = 0; i < 4; ++i) voff[i] = uint32_t(((4 * c + i) * row_stride + EPL * n) * 2);
+  const uint32_t vmask = uint32_t(EPL * n * 2);
 
   struct Regs {
     uint4 k[KSTEPS];
@@ -383,15 +402,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       r.k[j] = *reinterpret_cast<const uint4*>(kb + (kvalid ? koff[j] : kmask[j]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = tc + 4 * c + i < t1 ? voff[i] : vmask[i];
+      const uint32_t off = tc + 4 * c + i < t1 ? voff[i] : vmask;
       if constexpr (VW == 4) {
-        uint4 x = *reinterpret_cast<const uint4*>(vb + off);
+        const uint4 x = *reinterpret_cast<const uint4*>(vb + off);
         r.v[i][0] = x.x;
         r.v[i][1] = x.y;
         r.v[i][2] = x.z;
         r.v[i][3] = x.w;
       } else {
-        uint2 x = *reinterpret_cast<const uint2*>(vb + off);
+        const uint2 x = *reinterpret_cast<const uint2*>(vb + off);
         r.v[i][0] = x.x;
         r.v[i][1] = x.y;
       }
@@ -406,31 +425,40 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
                                                   __builtin_bit_cast(bf16x8_t, qop[j]), s, 0, 0,
                                                   0);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = tc + 4 * c + i < t1 ? s[i] * a.scale_log2 : -INFINITY;
+    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (__ballot(mx > m + kLazyMax)) {  // rare: move the reference max
+      float hm = fmaxf(mx, __shfl_xor(mx, 16));
+      hm = fmaxf(hm, __shfl_xor(hm, 32));
+      const float mn = hm > m + kLazyMax ? hm : m;
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
+      m = mn;
+    }
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = tc + 4 * c + i < t1 ? s[i] * a.scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    const uint32_t p01 = pack_bf16x2(p[0], p[1]);
+    const uint32_t p23 = pack_bf16x2(p[2], p[3]);
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(p[i] - mn);
-    float ps = (p[0] + p[1]) + (p[2] + p[3]);
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l = l * alpha + ps;
-    m = mn;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) acc[j] *= alpha;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const uint32_t w = r.v[i][j >> 1];
-        const float v = (j & 1) ? bf16_hi(w) : bf16_lo(w);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[i], acc[j], 0, 0, 0);
+    for (int t = 0; t < EPL; ++t) {
+      const int w = t >> 1;
+      uint32_t lo, hi;  // element t of rows 4c..4c+3, as bf16 pairs
+      if (t & 1) {
+        lo = (r.v[0][w] >> 16) | (r.v[1][w] & 0xFFFF0000u);
+        hi = (r.v[2][w] >> 16) | (r.v[3][w] & 0xFFFF0000u);
+      } else {
+        lo = (r.v[0][w] & 0xFFFFu) | (r.v[1][w] << 16);
+        hi = (r.v[2][w] & 0xFFFFu) | (r.v[3][w] << 16);
       }
+      const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pb, acc[t], 0, 0, 0);
     }
   };
 
@@ -453,8 +481,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       if (ch >= c_end) break;
     }
   }
+  // the four lanes of head n hold partial sums of the same reference max
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
 
-  // acc[j][r] = O[head n][EPL*(4c + r) + j] (unnormalised, this wave's tokens).
+  // acc[t][r] = O[head n][EPL*(4c + r) + t] (unnormalised, this wave's tokens).
   const bool single = nparts == 1;
   const size_t head0 = size_t(b) * Hq + size_t(kvh) * G;
   auto finish = [&](int h, int d, float o, float mm, float ll) {
@@ -474,7 +505,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) finish(n, EPL * (4 * c + r) + j, acc[j][r], m, l);
+        for (int t = 0; t < EPL; ++t) finish(n, EPL * (4 * c + r) + t, acc[t][r], m, l);
     }
   } else {
     __shared__ float s_o[NW][16][D];
@@ -482,7 +513,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) s_o[wave][n][EPL * (4 * c + r) + j] = acc[j][r];
+      for (int t = 0; t < EPL; ++t) s_o[wave][n][EPL * (4 * c + r) + t] = acc[t][r];
     if (c == 0) {
       s_ml[wave][n][0] = m;
       s_ml[wave][n][1] = l;
@@ -573,11 +604,12 @@ int g_decode_path = PKV_PATH_AUTO;
 // Matrix cores for bf16 groups of 4..16 query heads per kv head (and for the
 // group sizes the vector kernel is not built for); vector ALUs otherwise.
 bool use_mfma(bool bf16, int G) {
-  if (!bf16 || G < 2) return false;
-  const bool valu_ok = G == 2 || G == 4 || G == 8;
+  if (!bf16) return false;
+  const bool valu_ok = G == 1 || G == 2 || G == 4 || G == 8;
   if (g_decode_path == PKV_PATH_VALU && valu_ok) return false;
   if (g_decode_path == PKV_PATH_MFMA) return true;
-  return G >= 4 || !valu_ok;
+  if (g_decode_path == PKV_PATH_AUTO) return G >= 4 || !valu_ok;
+  return false;
 }
 
 template <typename T, int D, int BS>

@@ -218,3 +218,38 @@ def test_cache_write_rejects_bad_arguments(kw, code):
 def test_copy_blocks_rejects_bad_arguments():
     assert P.lib.pkv_copy_blocks(1, 1, 1, -1, 4, 16, 2, 64, P.BF16, None) == -1
     assert P.lib.pkv_copy_blocks(1, 1, 1, 0, 4, 16, 2, 64, P.BF16, None) == 0
+
+
+def test_decode_step_prepare_matches_oracle():
+    """One call per decode step (append one token to each sequence, then the
+    tables): same slots, tables and lengths as the oracle allocator, and
+    all-or-nothing on failure."""
+    s = W.shape(2)
+    wl = W.make_workload(s, with_payload=False, extra_tokens=40)
+    o, p = _both(wl.num_blocks, s.block_size, wl.free_order)
+    o.replay(wl.ops)
+    p.replay(wl.ops)
+    seqs = np.arange(s.num_seqs, dtype=np.int64)
+    mb = int(((wl.ctx + 40 + s.block_size - 1) // s.block_size).max())
+    slots = np.empty(s.num_seqs, np.int64)
+    tb = np.empty((s.num_seqs, mb), np.int32)
+    cx = np.empty(s.num_seqs, np.int32)
+    for step in range(20):
+        mx = p.decode_step_prepare(seqs, mb, slots, tb, cx)
+        ref_slots = [o.append(int(b), 1)[0] for b in seqs]
+        ref_t, ref_c = o.build_block_tables(list(seqs), mb)
+        assert list(slots) == ref_slots
+        assert np.array_equal(tb, ref_t) and np.array_equal(cx, ref_c)
+        assert mx == int(ref_c.max())
+    free = p.num_free_blocks()
+    with pytest.raises(P.PkvError) as e:
+        p.decode_step_prepare(np.array([0, 1, 0], np.int64), mb, slots, tb, cx)
+    assert e.value.code == "INVALID_ARG"
+    with pytest.raises(P.PkvError) as e:
+        p.decode_step_prepare(seqs, 1, slots, tb[:, :1].copy(), cx)
+    assert e.value.code == "INVALID_ARG"
+    with pytest.raises(P.PkvError) as e:
+        p.decode_step_prepare(np.array([0, 10 ** 6], np.int64), mb, slots, tb, cx)
+    assert e.value.code == "NOT_FOUND"
+    assert p.num_free_blocks() == free
+    _same_state(o, p, list(range(s.num_seqs)), s.block_size)

@@ -74,11 +74,11 @@ def decode_path():
     P.set_decode_path(P.PATH_AUTO)
 
 
-@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 @pytest.mark.parametrize("path", [P.PATH_VALU, P.PATH_MFMA])
 @pytest.mark.parametrize("part", [0, P.PARTITION_AUTO])
-def test_grouped_query_both_kernels(cfg, path, part, decode_path):
-    """The vector and matrix-core kernels on the grouped-query shapes."""
+def test_both_kernels(cfg, path, part, decode_path):
+    """The vector and matrix-core kernels on every bf16 shape."""
     decode_path(path)
     s = SMALL[cfg]
     log(f"{s.name} path={path} partition={part}")
@@ -111,7 +111,7 @@ def test_edge_lengths(dtype, D, bs, hq, hkv, part, decode_path):
                       ctx_fixed=EDGE_CTX, seed=77)
     st = build_step(s, poison=True, pad=-123456)
     ref = oracle_full(st)
-    paths = [P.PATH_VALU, P.PATH_MFMA] if dtype == "bf16" and hq > hkv else [P.PATH_AUTO]
+    paths = [P.PATH_VALU, P.PATH_MFMA] if dtype == "bf16" else [P.PATH_AUTO]
     for path in paths:
         decode_path(path)
         log(f"edge lengths {dtype} D={D} bs={bs} G={hq // hkv} partition={part} path={path}")
@@ -120,14 +120,18 @@ def test_edge_lengths(dtype, D, bs, hq, hkv, part, decode_path):
         assert_close(got, ref, dtype, f"edges {dtype} D{D} bs{bs} G{hq // hkv} p{part} path{path}")
 
 
-@pytest.mark.parametrize("cfg", [0, 2, 4])
-def test_peaked_softmax(cfg):
-    """q scaled by 8: the softmax is far from flat, so an indexing slip cannot
-    hide under averaging."""
-    s = {0: SMALL[0], 2: SMALL[2], 4: SMALL[4]}[cfg]
-    st = build_step(s, poison=True, q_scale=8.0)
-    for part in (0, P.PARTITION_AUTO):
-        assert_close(run_decode(st, part), oracle_full(st), s.dtype, f"{s.name} peaked p{part}")
+@pytest.mark.parametrize("cfg", [0, 2, 3, 4])
+def test_peaked_softmax(cfg, decode_path):
+    """q scaled by 8 (and 32): the softmax is far from flat, so an indexing
+    slip cannot hide under averaging, and the running maximum moves often."""
+    s = {0: SMALL[0], 2: SMALL[2], 3: SMALL[3], 4: SMALL[4]}[cfg]
+    for qs in (8.0, 32.0):
+        st = build_step(s, poison=True, q_scale=qs)
+        ref = oracle_full(st)
+        for path in ([P.PATH_AUTO] if s.dtype == "f32" else [P.PATH_VALU, P.PATH_MFMA]):
+            decode_path(path)
+            for part in (0, P.PARTITION_AUTO):
+                assert_close(run_decode(st, part), ref, s.dtype, f"{s.name} q*{qs} p{part} path{path}")
 
 
 def test_placement_invariance_on_gpu():
