@@ -39,6 +39,8 @@ def _args():
     ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 single pass, else tokens")
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto",
                     help="decode kernel: automatic choice, vector ALUs or matrix cores")
+    ap.add_argument("--staging-depth", type=int, default=8,
+                    help="pinned staging buffers in flight (steps the host may run ahead)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -250,20 +252,20 @@ def main() -> int:
     # One pinned staging buffer per in-flight step, laid out as the device
     # buffer it is copied to: slots int64 [B] | tables int32 [B, max_blocks] |
     # context lengths int32 [B].  One H2D copy per step.
-    nbuf = 2
+    nbuf = args.staging_depth  # the host waits only for copies this many steps back
     n_slot_b, n_tab_b, n_ctx_b = 8 * B, 4 * B * max_blocks, 4 * B
     stage_bytes = n_slot_b + n_tab_b + n_ctx_b
+    stage_bytes = (stage_bytes + 15) // 16 * 16
     h_stage = [torch.empty(stage_bytes, dtype=torch.uint8).pin_memory() for _ in range(nbuf)]
-    h_views = []
-    for hs in h_stage:
-        a_ = hs.numpy()
-        h_views.append((a_[:n_slot_b].view(np.int64),
-                        a_[n_slot_b:n_slot_b + n_tab_b].view(np.int32).reshape(B, max_blocks),
-                        a_[n_slot_b + n_tab_b:].view(np.int32)))
+    h_flat = [hs.numpy() for hs in h_stage]
+    host_flat = np.zeros(stage_bytes, dtype=np.uint8)  # ordinary memory, same layout
+    host_sl = host_flat[:n_slot_b].view(np.int64)
+    host_tb = host_flat[n_slot_b:n_slot_b + n_tab_b].view(np.int32).reshape(B, max_blocks)
+    host_cx = host_flat[n_slot_b + n_tab_b:n_slot_b + n_tab_b + n_ctx_b].view(np.int32)
     d_stage = torch.empty(stage_bytes, dtype=torch.uint8, device=dev)
     d_slots = d_stage[:n_slot_b].view(torch.int64)
     d_tables = d_stage[n_slot_b:n_slot_b + n_tab_b].view(torch.int32).view(B, max_blocks)
-    d_ctx = d_stage[n_slot_b + n_tab_b:].view(torch.int32)
+    d_ctx = d_stage[n_slot_b + n_tab_b:n_slot_b + n_tab_b + n_ctx_b].view(torch.int32)
     copied = [torch.cuda.Event() for _ in range(nbuf)]
     stream = torch.cuda.current_stream()
     new_k_steps = [new_k[i] for i in range(total_steps)] if step_new else None
@@ -286,19 +288,27 @@ def main() -> int:
           for _ in range(total_steps)]
     ctx_hist = []
     host_s = []
+    wait_s = []
 
     def step(i):
-        t_h = time.perf_counter()
+        t_w = time.perf_counter()
         j = i % nbuf
         if i >= nbuf:
             copied[j].synchronize()  # staging buffer j is free again
-        sl, tb, cx = h_views[j]
+        t_h = time.perf_counter()
+        wait_s.append(t_h - t_w)
+        # The allocator writes into ordinary (cached) host memory; one bulk
+        # copy then moves the step's slots, tables and lengths into the pinned
+        # staging buffer, which is uncached and never read back by the host.
+        cx = np.empty(B, np.int32)
         if step_new:
-            maxc = alloc.decode_step_prepare(seqs, max_blocks, sl, tb, cx)
+            maxc = alloc.decode_step_prepare(seqs, max_blocks, host_sl, host_tb, cx)
         else:
-            alloc.build_block_tables(seqs, max_blocks, pad=-1, tables_out=tb, ctx_out=cx)
+            alloc.build_block_tables(seqs, max_blocks, pad=-1, tables_out=host_tb, ctx_out=cx)
             maxc = int(cx.max())
-        d_stage.copy_(h_stage[j], non_blocking=True)
+        host_cx[:] = cx
+        np.copyto(h_flat[j], host_flat)
+        P.upload_pinned(d_stage, h_stage[j])
         copied[j].record(stream)
         if step_new:
             P.kv_reshape_and_cache(new_k_steps[i], new_v_steps[i], k_cache, v_cache, d_slots)
@@ -306,7 +316,7 @@ def main() -> int:
         P.paged_attention_decode(out, q, k_cache, v_cache, d_tables, d_ctx, maxc, s.scale,
                                  args.partition, workspace)
         ev[i][1].record(stream)
-        ctx_hist.append(cx.copy())
+        ctx_hist.append(cx)
         host_s.append(time.perf_counter() - t_h)
 
     for i in range(args.warmup):
@@ -348,6 +358,7 @@ def main() -> int:
         "seq_tokens_per_s": round(tok_t / elapsed, 1),
         "decode_tokens_per_s": round(B * K / elapsed, 1),
         "host_us_per_step": round(float(np.mean(host_s[timed])) * 1e6, 1),
+        "host_wait_us_per_step": round(float(np.mean(wait_s[timed])) * 1e6, 1),
         "config": {
             "workload": s.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": bs, "mean_context": round(tok_t / K / B, 1),

@@ -183,6 +183,19 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
                            int32_t head_dim, pkv_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Host-to-device staging by the GPU: copies `bytes` from pinned host memory
+ * (allocated pinned and mapped into the device's address space, e.g. a torch
+ * tensor from pin_memory()) to device memory, as a kernel on `stream`.  Used
+ * for each decode step's tables, lengths and slots: the launch is queued like
+ * any kernel and never waits for earlier work, unlike a runtime copy that may
+ * block the host.  The caller must not rewrite `src_host` until the copy has
+ * run (e.g. a ring of staging buffers guarded by events).
+ * bytes and both addresses must be multiples of 16; PKV_ERR_INVALID_ARG if
+ * the source is not pinned, mapped host memory (nothing is launched).
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_upload_pinned(void* dst, const void* src_host, size_t bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block allocator (host memory only; single-threaded use).
  *
  * Fixed-size blocks are handed out one at a time as a sequence grows; a

@@ -18,7 +18,7 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "lib", "PkvError", "F32", "BF16", "PARTITION_AUTO",
     "kv_reshape_and_cache", "paged_attention_decode", "decode_workspace_bytes",
-    "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path",
+    "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned",
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
 ]
 
@@ -50,6 +50,7 @@ EXPORTS = {
                                           _vp]),
     "pkv_set_decode_path": (_i32, [_i32]),
     "pkv_get_decode_path": (_i32, []),
+    "pkv_upload_pinned": (_i32, [_vp, _vp, _sz, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_allocator_create": (_i32, [_i32, _i32, _P(_i32), _P(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
@@ -161,6 +162,16 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
         int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
         ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode")
+
+
+def upload_pinned(dst, src_pinned, stream=None) -> None:
+    """Copy a pinned host tensor into a device tensor with a GPU kernel on the
+    stream (never blocks the host); sizes must match, multiples of 16 bytes."""
+    n = src_pinned.numel() * src_pinned.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("upload_pinned: size mismatch")
+    _check(lib.pkv_upload_pinned(dst.data_ptr(), src_pinned.data_ptr(), n, _stream_ptr(stream)),
+           "upload_pinned")
 
 
 def set_decode_path(path: int) -> None:

@@ -254,9 +254,15 @@ extern "C" pkv_status pkv_decode_step_prepare(pkv_allocator* a, const int64_t* s
   st = pkv_build_block_tables(a, seq_ids, num_seqs, max_blocks_per_seq, pad_value, tables_out,
                               context_lens_out);
   if (st != PKV_OK) return st;  // cannot happen: checked above
-  int32_t mx = 0;
-  if (context_lens_out)
-    for (int32_t i = 0; i < num_seqs; ++i) mx = context_lens_out[i] > mx ? context_lens_out[i] : mx;
-  if (max_context_len_out) *max_context_len_out = mx;
+  if (max_context_len_out) {
+    // from the allocator's own state: the output arrays may be pinned,
+    // uncached host memory that is slow to read back
+    int64_t mx = 0;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int64_t len = a->seqs.find(seq_ids[i])->second.len;
+      mx = len > mx ? len : mx;
+    }
+    *max_context_len_out = int32_t(mx);
+  }
   return pkv::ok();
 }

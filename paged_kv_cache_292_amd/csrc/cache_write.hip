@@ -9,6 +9,7 @@
 // is one contiguous copy of num_kv_heads * head_dim elements per cache.
 // Block copies give a sequence its own copy of a block that others still
 // share ("What Is vLLM …", section "How does PagedAttention work?").
+#include <algorithm>
 #include <cstdint>
 
 #include "pkv_internal.h"
@@ -49,6 +50,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
   const uint4* s = c + src * block_vec;
   uint4* d = c + dst * block_vec;
   for (int64_t j = threadIdx.x; j < block_vec; j += blockDim.x) d[j] = s[j];
+}
+
+// Copy of mapped pinned host memory into device memory by the GPU itself.
+__global__ __launch_bounds__(256) void upload_kernel(const uint4* __restrict__ src,
+                                                     uint4* __restrict__ dst, int64_t n_vec) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n_vec;
+       i += int64_t(gridDim.x) * 256)
+    dst[i] = src[i];
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -126,5 +135,30 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int64_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(PKV_ERR_HIP, "copy_blocks: launch failed: %s", hipGetErrorString(e));
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_upload_pinned(void* dst, const void* src_host, size_t bytes,
+                                        void* stream) {
+  if (bytes == 0) return pkv::ok();
+  if (!dst || !src_host)
+    return fail(PKV_ERR_INVALID_ARG, "upload_pinned: NULL pointer argument");
+  if (bytes % 16 || !pkv::aligned16(dst) || !pkv::aligned16(src_host))
+    return fail(PKV_ERR_INVALID_ARG,
+                "upload_pinned: size (%zu) and both addresses must be multiples of 16 bytes", bytes);
+  void* src_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(src_host), 0);
+  if (e != hipSuccess || !src_dev)
+    return fail(PKV_ERR_INVALID_ARG,
+                "upload_pinned: source is not pinned, device-mapped host memory (%s)",
+                hipGetErrorString(e));
+  const int64_t n_vec = int64_t(bytes / 16);
+  const int64_t blocks = std::min<int64_t>((n_vec + 255) / 256, 1024);
+  hipLaunchKernelGGL(pkv::upload_kernel, dim3(unsigned(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src_dev),
+                     static_cast<uint4*>(dst), n_vec);
+  e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "upload_pinned: launch failed: %s", hipGetErrorString(e));
   return pkv::ok();
 }

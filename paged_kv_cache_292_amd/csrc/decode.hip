@@ -31,6 +31,34 @@ namespace {
 
 using namespace dev;
 
+// Workgroup -> (partition, kv head, sequence).  The dispatcher deals
+// consecutive workgroups round-robin to the 8 XCDs.  Partitions of one
+// sequence are kept adjacent (they read neighbouring blocks of the same
+// table), and the partition dimension of the grid is odd, so the partitions
+// of consecutive (head, sequence) pairs rotate over the XCDs instead of
+// partition p always landing on XCD p mod 8.  Columns past the partition
+// count are empty and exit at once.
+#ifndef PKV_GRID_ORDER
+#define PKV_GRID_ORDER 1
+#endif
+#if PKV_GRID_ORDER == 1
+#define WORK_ITEM_COORDS                 \
+  const int part = blockIdx.x;           \
+  const int kvh = blockIdx.y;            \
+  const int b = blockIdx.z;
+__host__ __device__ inline dim3 work_grid(int parts, int kv_heads, int seqs) {
+  return dim3(parts | 1, kv_heads, seqs);
+}
+#else
+#define WORK_ITEM_COORDS                 \
+  const int kvh = blockIdx.x;            \
+  const int b = blockIdx.y;              \
+  const int part = gridDim.z - 1 - blockIdx.z;
+__host__ __device__ inline dim3 work_grid(int parts, int kv_heads, int seqs) {
+  return dim3(kv_heads, seqs, parts);
+}
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 16;          // tokens per wave iteration
 constexpr int kSingle = 1 << 30;    // "partition" length of single-pass mode
@@ -71,9 +99,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4;
   const int r = lane & 15;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  WORK_ITEM_COORDS
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
 
@@ -329,9 +355,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane >> 4;
   const int n = lane & 15;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  WORK_ITEM_COORDS
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
@@ -586,14 +610,14 @@ constexpr int kNW = PKV_DECODE_WAVES;  // waves per workgroup
 
 template <typename T, int D, int BS, int G>
 hipError_t launch_valu(const DecodeArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
-  dim3 grid(grid_parts, a.num_kv_heads, num_seqs);
+  const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
   hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kNW>), grid, dim3(kNW * 64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D, int BS>
 hipError_t launch_mfma(const DecodeArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
-  dim3 grid(grid_parts, a.num_kv_heads, num_seqs);
+  const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
   hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW>), grid, dim3(kNW * 64), 0, st, a);
   return hipGetLastError();
 }
@@ -771,6 +795,10 @@ extern "C" pkv_status pkv_paged_attention_decode(
     a.part_ml = ws + size_t(num_seqs) * num_q_heads * a.max_parts * head_dim;
     grid_parts = int((int64_t(cap) + partition - 1) / partition);
     if (grid_parts < 1) grid_parts = 1;
+    if (grid_parts > 65535)
+      return fail(PKV_ERR_INVALID_ARG,
+                  "paged_attention_decode: %d partitions of %d tokens exceed the grid limit",
+                  grid_parts, partition);
   } else {
     a.partition = pkv::kSingle;
     a.max_parts = 1;

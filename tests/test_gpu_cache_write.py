@@ -79,3 +79,17 @@ def test_copy_blocks():
         ve[d_] = vc[s_]
     assert np.array_equal(from_dev(kd, "bf16"), ke)
     assert np.array_equal(from_dev(vd, "bf16"), ve)
+
+
+def test_upload_pinned():
+    """The GPU-side copy of a pinned staging buffer is bit-exact, and pageable
+    host memory is refused before anything is launched."""
+    n = 4096 * 37 + 16
+    src = torch.from_numpy(W.normal_bf16_bits(3, 3, n // 2).view(np.uint8).copy()).pin_memory()
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    P.upload_pinned(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), src)
+    with pytest.raises(P.PkvError) as e:
+        P.upload_pinned(dst[:32], torch.zeros(32, dtype=torch.uint8))
+    assert e.value.code == "INVALID_ARG"
