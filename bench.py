@@ -2,10 +2,11 @@
 """Benchmark: one PagedAttention decode step on one MI355X.
 
 A step is the whole hot path over one synthetic batch: the host allocator
-appends one token per sequence (slot mapping), rebuilds the block tables and
-context lengths, copies them to the device, the cache write stores the new
-tokens' K/V, and paged decode attention (with its partition merge) runs over
-every sequence's full context.  Inputs are resident in HBM before timing.
+appends one token per sequence (slot mapping), rebuilds the block tables,
+context lengths and the longest-first launch order into a pinned staging
+buffer that a GPU kernel uploads, the cache write stores the new tokens' K/V,
+and paged decode attention (with its partition merge) runs over every
+sequence's full context.  Inputs are resident in HBM before timing.
 
 Default workload: the LLaMA-13B-shaped decode layer (128 sequences, 40 heads
 of 128, bf16 KV, block 16, log-normal context lengths with median 600 clipped
@@ -39,6 +40,8 @@ def _args():
     ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 single pass, else tokens")
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto",
                     help="decode kernel: automatic choice, vector ALUs or matrix cores")
+    ap.add_argument("--order", choices=["longest", "index"], default="longest",
+                    help="launch order of the sequences handed to the decode kernel")
     ap.add_argument("--staging-depth", type=int, default=8,
                     help="pinned staging buffers in flight (steps the host may run ahead)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
@@ -253,19 +256,23 @@ def main() -> int:
     # buffer it is copied to: slots int64 [B] | tables int32 [B, max_blocks] |
     # context lengths int32 [B].  One H2D copy per step.
     nbuf = args.staging_depth  # the host waits only for copies this many steps back
-    n_slot_b, n_tab_b, n_ctx_b = 8 * B, 4 * B * max_blocks, 4 * B
-    stage_bytes = n_slot_b + n_tab_b + n_ctx_b
+    n_slot_b, n_tab_b, n_ctx_b, n_ord_b = 8 * B, 4 * B * max_blocks, 4 * B, 4 * B
+    stage_bytes = n_slot_b + n_tab_b + n_ctx_b + n_ord_b
     stage_bytes = (stage_bytes + 15) // 16 * 16
     h_stage = [torch.empty(stage_bytes, dtype=torch.uint8).pin_memory() for _ in range(nbuf)]
     h_flat = [hs.numpy() for hs in h_stage]
     host_flat = np.zeros(stage_bytes, dtype=np.uint8)  # ordinary memory, same layout
     host_sl = host_flat[:n_slot_b].view(np.int64)
     host_tb = host_flat[n_slot_b:n_slot_b + n_tab_b].view(np.int32).reshape(B, max_blocks)
-    host_cx = host_flat[n_slot_b + n_tab_b:n_slot_b + n_tab_b + n_ctx_b].view(np.int32)
+    o_cx = n_slot_b + n_tab_b
+    host_cx = host_flat[o_cx:o_cx + n_ctx_b].view(np.int32)
+    host_ord = host_flat[o_cx + n_ctx_b:o_cx + n_ctx_b + n_ord_b].view(np.int32)
     d_stage = torch.empty(stage_bytes, dtype=torch.uint8, device=dev)
     d_slots = d_stage[:n_slot_b].view(torch.int64)
     d_tables = d_stage[n_slot_b:n_slot_b + n_tab_b].view(torch.int32).view(B, max_blocks)
-    d_ctx = d_stage[n_slot_b + n_tab_b:n_slot_b + n_tab_b + n_ctx_b].view(torch.int32)
+    d_ctx = d_stage[o_cx:o_cx + n_ctx_b].view(torch.int32)
+    d_order = d_stage[o_cx + n_ctx_b:o_cx + n_ctx_b + n_ord_b].view(torch.int32)
+    use_order = args.order == "longest"
     copied = [torch.cuda.Event() for _ in range(nbuf)]
     stream = torch.cuda.current_stream()
     new_k_steps = [new_k[i] for i in range(total_steps)] if step_new else None
@@ -302,10 +309,13 @@ def main() -> int:
         # staging buffer, which is uncached and never read back by the host.
         cx = np.empty(B, np.int32)
         if step_new:
-            maxc = alloc.decode_step_prepare(seqs, max_blocks, host_sl, host_tb, cx)
+            maxc = alloc.decode_step_prepare(seqs, max_blocks, host_sl, host_tb, cx,
+                                             order_out=host_ord if use_order else None)
         else:
             alloc.build_block_tables(seqs, max_blocks, pad=-1, tables_out=host_tb, ctx_out=cx)
             maxc = int(cx.max())
+            if use_order:
+                host_ord[:] = P.longest_first_order(cx)
         host_cx[:] = cx
         np.copyto(h_flat[j], host_flat)
         P.upload_pinned(d_stage, h_stage[j])
@@ -314,7 +324,8 @@ def main() -> int:
             P.kv_reshape_and_cache(new_k_steps[i], new_v_steps[i], k_cache, v_cache, d_slots)
         ev[i][0].record(stream)
         P.paged_attention_decode(out, q, k_cache, v_cache, d_tables, d_ctx, maxc, s.scale,
-                                 args.partition, workspace)
+                                 args.partition, workspace,
+                                 seq_order=d_order if use_order else None)
         ev[i][1].record(stream)
         ctx_hist.append(cx)
         host_s.append(time.perf_counter() - t_h)
@@ -364,7 +375,7 @@ def main() -> int:
             "head_dim": D, "block_size": bs, "mean_context": round(tok_t / K / B, 1),
             "max_context": max_ctx_final, "new_tokens_per_step": B * step_new,
             "partition_size": part_used, "kv_bytes_per_step": int(kv_t // K),
-            "decode_path": args.path,
+            "decode_path": args.path, "launch_order": args.order,
         },
         "roofline": {
             "kernel": "paged_attention_decode (partition kernel + log-sum-exp merge)",

@@ -117,6 +117,13 @@ pkv_status pkv_kv_reshape_and_cache(const void* key, const void* value,
  *               faulting, and the result is meaningless).
  * context_lens  device, int32 [num_seqs]; each value is clamped to
  *               [0, min(max_context_len, max_blocks_per_seq * block_size)].
+ * seq_order     device, int32 [num_seqs] or NULL: the order in which the
+ *               sequences' work is started, a permutation of 0..num_seqs-1
+ *               (pkv_longest_first_order gives longest first, which keeps
+ *               the longest sequences from finishing last).  It changes only
+ *               the speed; NULL = index order.  An entry outside the range
+ *               is treated as its own index (no out-of-bounds access, but
+ *               a non-permutation leaves some rows unwritten).
  * max_context_len  host-side upper bound of context_lens (sizes the grid).
  * workspace     device scratch of at least pkv_decode_workspace_bytes(...)
  *               bytes when partitions are used (may be NULL otherwise).
@@ -160,6 +167,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q,
                                       const int32_t* block_tables,
                                       int32_t max_blocks_per_seq,
                                       const int32_t* context_lens,
+                                      const int32_t* seq_order,
                                       int32_t max_context_len, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t num_kv_heads,
                                       int32_t head_dim, int32_t block_size,
@@ -249,11 +257,18 @@ pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64_t* seq_ids
                                   int32_t pad_value, int32_t* tables_out,
                                   int32_t* context_lens_out);
 
+/* Host helper: order_out (host int32 [n]) receives 0..n-1 sorted by
+ * context_lens (host int32 [n]) descending, ties by index — the launch order
+ * pkv_paged_attention_decode's seq_order expects. */
+pkv_status pkv_longest_first_order(const int32_t* context_lens, int32_t n, int32_t* order_out);
+
 /* One decode step's host work in one call: every sequence in seq_ids grows
  * by one token (slots_out, host int64 [num_seqs], receives the new slots in
  * order), then tables_out (host int32 [num_seqs, max_blocks_per_seq]) and
  * context_lens_out (host int32 [num_seqs]) receive the grown tables and
- * lengths, and *max_context_len_out their maximum (either may be NULL).
+ * lengths, *max_context_len_out their maximum and order_out (host int32
+ * [num_seqs]) the longest-first launch order (any of the last three may be
+ * NULL).
  * seq_ids must be distinct.  All-or-nothing: PKV_ERR_NOT_FOUND,
  * PKV_ERR_INVALID_ARG (a repeated id, or a table that would not fit),
  * PKV_ERR_OUT_OF_BLOCKS or PKV_ERR_SHARED_WRITE leave the allocator
@@ -262,7 +277,7 @@ pkv_status pkv_decode_step_prepare(pkv_allocator* a, const int64_t* seq_ids,
                                    int32_t num_seqs, int32_t max_blocks_per_seq,
                                    int32_t pad_value, int64_t* slots_out,
                                    int32_t* tables_out, int32_t* context_lens_out,
-                                   int32_t* max_context_len_out);
+                                   int32_t* max_context_len_out, int32_t* order_out);
 
 int32_t pkv_num_free_blocks(const pkv_allocator* a);
 /* Reference count of a block (0 = free), -1 for an id outside the pool. */

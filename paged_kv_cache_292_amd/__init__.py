@@ -18,7 +18,7 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "lib", "PkvError", "F32", "BF16", "PARTITION_AUTO",
     "kv_reshape_and_cache", "paged_attention_decode", "decode_workspace_bytes",
-    "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned",
+    "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned", "longest_first_order",
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
 ]
 
@@ -45,9 +45,10 @@ EXPORTS = {
                                         _i64, _i64, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
-    "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
-                                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
-                                          _vp]),
+    "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
+                                          _i32, _vp]),
+    "pkv_longest_first_order": (_i32, [_P(_i32), _i32, _P(_i32)]),
     "pkv_set_decode_path": (_i32, [_i32]),
     "pkv_get_decode_path": (_i32, []),
     "pkv_upload_pinned": (_i32, [_vp, _vp, _sz, _vp]),
@@ -61,7 +62,7 @@ EXPORTS = {
     "pkv_seq_free": (_i32, [_vp, _i64]),
     "pkv_build_block_tables": (_i32, [_vp, _P(_i64), _i32, _i32, _i32, _P(_i32), _P(_i32)]),
     "pkv_decode_step_prepare": (_i32, [_vp, _P(_i64), _i32, _i32, _i32, _P(_i64), _P(_i32),
-                                       _P(_i32), _P(_i32)]),
+                                       _P(_i32), _P(_i32), _P(_i32)]),
     "pkv_num_free_blocks": (_i32, [_vp]),
     "pkv_block_refcount": (_i32, [_vp, _i32]),
     "pkv_seq_context_len": (_i64, [_vp, _i64]),
@@ -132,6 +133,16 @@ def kv_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None
         _dtype_code(k_cache), _stream_ptr(stream)), "kv_reshape_and_cache")
 
 
+def longest_first_order(context_lens) -> np.ndarray:
+    """Host: indices sorted by context length, longest first (ties by index)."""
+    c = np.ascontiguousarray(context_lens, dtype=np.int32)
+    out = np.empty(len(c), dtype=np.int32)
+    _check(lib.pkv_longest_first_order(c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(c),
+                                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+           "longest_first_order")
+    return out
+
+
 def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_context_len, partition_size=PARTITION_AUTO, dtype=BF16) -> int:
     return int(lib.pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -148,11 +159,13 @@ def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                            max_context_len: int, scale: float,
                            partition_size: int = PARTITION_AUTO, workspace=None,
-                           stream=None) -> None:
+                           stream=None, seq_order=None) -> None:
     """``out[b, h] = softmax(scale · K_b q[b, h]) V_b`` through the block tables.
 
     ``workspace`` is a device byte tensor of at least
-    ``decode_workspace_bytes(...)`` bytes when partitions are used."""
+    ``decode_workspace_bytes(...)`` bytes when partitions are used;
+    ``seq_order`` an optional device int32 launch order (longest first is
+    fastest, see ``longest_first_order``)."""
     N, bs, Hkv, D = k_cache.shape
     B, Hq, _ = q.shape
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -160,7 +173,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _check(lib.pkv_paged_attention_decode(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
-        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
+        seq_order.data_ptr() if seq_order is not None else None, int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
         ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode")
 
 
@@ -264,16 +277,19 @@ class Allocator:
         return t, c
 
     def decode_step_prepare(self, seqs: np.ndarray, max_blocks: int, slots_out: np.ndarray,
-                            tables_out: np.ndarray, ctx_out: np.ndarray, pad: int = -1) -> int:
+                            tables_out: np.ndarray, ctx_out: np.ndarray, pad: int = -1,
+                            order_out: Optional[np.ndarray] = None) -> int:
         """Grow every sequence in ``seqs`` (int64) by one token and write the
-        new slots, the tables and context lengths into the given host arrays
-        (contiguous int64 / int32 / int32); returns the longest context."""
+        new slots, the tables, context lengths and (optionally) the
+        longest-first launch order into the given host arrays (contiguous
+        int64 / int32 / int32 / int32); returns the longest context."""
         mx = ctypes.c_int32(0)
+        po = ctypes.POINTER(ctypes.c_int32)
         _check(lib.pkv_decode_step_prepare(
             self._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(seqs), max_blocks,
             pad, slots_out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-            tables_out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-            ctx_out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(mx)),
+            tables_out.ctypes.data_as(po), ctx_out.ctypes.data_as(po), ctypes.byref(mx),
+            order_out.ctypes.data_as(po) if order_out is not None else None),
             "decode_step_prepare")
         return int(mx.value)
 

@@ -11,8 +11,10 @@
 // starts as the caller's free_order; a block whose count drops to zero joins
 // its tail.  Every operation checks all of its preconditions before changing
 // anything, so a failing call leaves the allocator as it was.
+#include <algorithm>
 #include <cstdint>
 #include <deque>
+#include <numeric>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -226,7 +228,7 @@ extern "C" pkv_status pkv_decode_step_prepare(pkv_allocator* a, const int64_t* s
                                               int32_t num_seqs, int32_t max_blocks_per_seq,
                                               int32_t pad_value, int64_t* slots_out,
                                               int32_t* tables_out, int32_t* context_lens_out,
-                                              int32_t* max_context_len_out) {
+                                              int32_t* max_context_len_out, int32_t* order_out) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "decode_step_prepare: NULL allocator");
   if (num_seqs < 0 || (num_seqs > 0 && (!seq_ids || !slots_out || !tables_out)))
     return fail(PKV_ERR_INVALID_ARG, "decode_step_prepare: bad arguments");
@@ -264,5 +266,22 @@ extern "C" pkv_status pkv_decode_step_prepare(pkv_allocator* a, const int64_t* s
     }
     *max_context_len_out = int32_t(mx);
   }
+  if (order_out) {
+    static thread_local std::vector<int32_t> lens;
+    lens.resize(size_t(num_seqs));
+    for (int32_t i = 0; i < num_seqs; ++i)
+      lens[size_t(i)] = int32_t(a->seqs.find(seq_ids[i])->second.len);
+    return pkv_longest_first_order(lens.data(), num_seqs, order_out);
+  }
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_longest_first_order(const int32_t* context_lens, int32_t n,
+                                              int32_t* order_out) {
+  if (n < 0 || (n > 0 && (!context_lens || !order_out)))
+    return fail(PKV_ERR_INVALID_ARG, "longest_first_order: bad arguments");
+  std::iota(order_out, order_out + n, 0);
+  std::stable_sort(order_out, order_out + n,
+                   [&](int32_t x, int32_t y) { return context_lens[x] > context_lens[y]; });
   return pkv::ok();
 }

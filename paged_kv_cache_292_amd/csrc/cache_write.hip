@@ -148,10 +148,12 @@ extern "C" pkv_status pkv_upload_pinned(void* dst, const void* src_host, size_t 
                 "upload_pinned: size (%zu) and both addresses must be multiples of 16 bytes", bytes);
   void* src_dev = nullptr;
   hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(src_host), 0);
-  if (e != hipSuccess || !src_dev)
+  if (e != hipSuccess || !src_dev) {
+    (void)hipGetLastError();  // leave no sticky runtime error for the caller's next call
     return fail(PKV_ERR_INVALID_ARG,
                 "upload_pinned: source is not pinned, device-mapped host memory (%s)",
                 hipGetErrorString(e));
+  }
   const int64_t n_vec = int64_t(bytes / 16);
   const int64_t blocks = std::min<int64_t>((n_vec + 255) / 256, 1024);
   hipLaunchKernelGGL(pkv::upload_kernel, dim3(unsigned(blocks)), dim3(256), 0,

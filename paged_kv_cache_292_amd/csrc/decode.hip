@@ -45,14 +45,14 @@ using namespace dev;
 #define WORK_ITEM_COORDS                 \
   const int part = blockIdx.x;           \
   const int kvh = blockIdx.y;            \
-  const int b = blockIdx.z;
+  const int b = seq_of(a, blockIdx.z);
 __host__ __device__ inline dim3 work_grid(int parts, int kv_heads, int seqs) {
   return dim3(parts | 1, kv_heads, seqs);
 }
 #else
 #define WORK_ITEM_COORDS                 \
   const int kvh = blockIdx.x;            \
-  const int b = blockIdx.y;              \
+  const int b = seq_of(a, blockIdx.y);   \
   const int part = gridDim.z - 1 - blockIdx.z;
 __host__ __device__ inline dim3 work_grid(int parts, int kv_heads, int seqs) {
   return dim3(kv_heads, seqs, parts);
@@ -70,8 +70,10 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* tables;
   const int32_t* ctx_lens;
+  const int32_t* order;  // optional launch order of the sequences (a permutation)
   float* part_o;   // [B, Hq, max_parts, D]
   float* part_ml;  // [B, Hq, max_parts, 2] (max in log2 units, sum)
+  int32_t num_seqs;
   int32_t max_blocks;
   int32_t ctx_cap;  // min(max_context_len, max_blocks * block_size)
   int32_t num_q_heads;
@@ -81,6 +83,15 @@ struct DecodeArgs {
   int32_t max_parts;
   float scale_log2;   // scale * log2(e): logits are kept in base-2 units
 };
+
+// Sequence handled by grid row z: the caller's launch order if given (e.g.
+// longest first, so the longest sequences do not finish last), else z.
+// Entries are clamped into range, so a bad order cannot read out of bounds.
+__device__ __forceinline__ int seq_of(const DecodeArgs& a, int z) {
+  if (!a.order) return z;
+  const int b = scalar_read(a.order + z);
+  return (unsigned)b < (unsigned)a.num_seqs ? b : z;
+}
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int b) {
   int c = a.ctx_lens[b];
@@ -604,7 +615,7 @@ __global__ __launch_bounds__(64) void reduce_partitions_kernel(DecodeArgs a) {
 #define PKV_DECODE_WAVES 4
 #endif
 #ifndef PKV_AUTO_PARTITION
-#define PKV_AUTO_PARTITION 512
+#define PKV_AUTO_PARTITION 2048
 #endif
 constexpr int kNW = PKV_DECODE_WAVES;  // waves per workgroup
 
@@ -670,11 +681,12 @@ bool group_supported(bool bf16, int g) {
   return bf16 && g >= 2 && g <= 16;
 }
 
-// Partition length actually used, 0 = single pass.  AUTO splits long
-// contexts into 512-token partitions.
+// Partition length actually used, 0 = single pass.  AUTO splits contexts
+// longer than 2048 tokens into 2048-token partitions (measured on MI355X over
+// the five decode shapes with a longest-first launch order).
 int32_t resolve_partition(int32_t max_context_len, int32_t partition_size) {
   if (partition_size == PKV_PARTITION_AUTO)
-    return max_context_len > 2 * PKV_AUTO_PARTITION ? PKV_AUTO_PARTITION : 0;
+    return max_context_len > PKV_AUTO_PARTITION ? PKV_AUTO_PARTITION : 0;
   return partition_size;
 }
 
@@ -721,7 +733,7 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
 extern "C" pkv_status pkv_paged_attention_decode(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
     void* stream) {
@@ -771,6 +783,8 @@ extern "C" pkv_status pkv_paged_attention_decode(
   a.v_cache = v_cache;
   a.tables = block_tables;
   a.ctx_lens = context_lens;
+  a.order = seq_order;
+  a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.ctx_cap = cap;
   a.num_q_heads = num_q_heads;

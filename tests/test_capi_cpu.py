@@ -176,7 +176,7 @@ def _decode(**kw):
     args.update(kw)
     return P.lib.pkv_paged_attention_decode(
         args["out"], args["q"], args["k"], args["v"], args["tables"], args["max_blocks"],
-        args["ctx"], args["max_ctx"], args["B"], args["Hq"], args["Hkv"], args["D"], args["bs"],
+        args["ctx"], None, args["max_ctx"], args["B"], args["Hq"], args["Hkv"], args["D"], args["bs"],
         args["N"], args["scale"], args["part"], args["ws"], args["ws_bytes"], args["dtype"],
         args["stream"])
 
@@ -234,8 +234,10 @@ def test_decode_step_prepare_matches_oracle():
     slots = np.empty(s.num_seqs, np.int64)
     tb = np.empty((s.num_seqs, mb), np.int32)
     cx = np.empty(s.num_seqs, np.int32)
+    order = np.empty(s.num_seqs, np.int32)
     for step in range(20):
-        mx = p.decode_step_prepare(seqs, mb, slots, tb, cx)
+        mx = p.decode_step_prepare(seqs, mb, slots, tb, cx, order_out=order)
+        assert np.array_equal(order, np.argsort(-cx, kind="stable"))
         ref_slots = [o.append(int(b), 1)[0] for b in seqs]
         ref_t, ref_c = o.build_block_tables(list(seqs), mb)
         assert list(slots) == ref_slots
@@ -253,3 +255,11 @@ def test_decode_step_prepare_matches_oracle():
     assert e.value.code == "NOT_FOUND"
     assert p.num_free_blocks() == free
     _same_state(o, p, list(range(s.num_seqs)), s.block_size)
+
+
+def test_longest_first_order():
+    c = np.array([5, 9, 9, 0, 100, 5, 7], np.int32)
+    assert P.longest_first_order(c).tolist() == [4, 1, 2, 6, 0, 5, 3]
+    assert P.longest_first_order(np.zeros(0, np.int32)).tolist() == []
+    r = W.random_lengths(3, 500, 0, 50).astype(np.int32)
+    assert np.array_equal(P.longest_first_order(r), np.argsort(-r, kind="stable"))

@@ -93,3 +93,5 @@ def test_upload_pinned():
     with pytest.raises(P.PkvError) as e:
         P.upload_pinned(dst[:32], torch.zeros(32, dtype=torch.uint8))
     assert e.value.code == "INVALID_ARG"
+    # the refusal leaves the runtime usable: the next torch call succeeds
+    torch.ones(4, device="cuda").sum().item()

@@ -151,3 +151,22 @@ def test_placement_invariance_on_gpu():
     b.tables_dev.copy_(torch.from_numpy(tb).cuda())
     got_b = run_decode(b, 0)
     np.testing.assert_array_equal(got_a, got_b)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_launch_order_does_not_change_results(cfg, decode_path):
+    """Longest-first and random launch orders give the same values as index
+    order, on both kernels (the order only changes which work starts first)."""
+    s = SMALL[cfg]
+    st = build_step(s, poison=True)
+    ref = oracle_full(st)
+    lf = P.longest_first_order(st.ctx)
+    rnd = W.permutation(cfg, s.num_seqs).astype(np.int32)
+    for path in (P.PATH_VALU, P.PATH_MFMA):
+        decode_path(path)
+        for part in (0, 64, P.PARTITION_AUTO):
+            base = run_decode(st, part)
+            for order in (lf, rnd):
+                got = run_decode(st, part, order)
+                np.testing.assert_array_equal(got, base)
+            assert_close(base, ref, s.dtype, f"{s.name} order p{part} path{path}")
