@@ -168,8 +168,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = tc + 4 * i + grp < t1 ? slot_off[i] : lane_off;
-      load_frag(kd[i], kb + off);
-      load_frag(vd[i], vb + off);
+      load_frag_stream(kd[i], kb + off);
+      load_frag_stream(vd[i], vb + off);
     }
   };
 
@@ -349,7 +349,20 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 
-constexpr float kLazyMax = 8.0f;  // log2 of the largest p allowed before rescaling
+constexpr float kLazyMax = 8.0f;
+
+// Load flavours of the matrix-core kernel.  Its V loads read whole 256-byte
+// rows per 16 lanes and stream them (non-temporal); its K loads read a 64-byte
+// quarter of each row per instruction, so they keep the normal caching that
+// lets the next instructions find the rest of the line.
+#ifndef PKV_MFMA_K_NT
+#define PKV_MFMA_K_NT 0
+#endif
+#ifndef PKV_MFMA_V_NT
+#define PKV_MFMA_V_NT 1
+#endif
+constexpr bool kMfmaKNT = PKV_MFMA_K_NT;
+constexpr bool kMfmaVNT = PKV_MFMA_V_NT;  // log2 of the largest p allowed before rescaling
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2v_t v = {lo, hi};
@@ -434,18 +447,18 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const bool kvalid = tc + n < t1;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j)
-      r.k[j] = *reinterpret_cast<const uint4*>(kb + (kvalid ? koff[j] : kmask[j]));
+      r.k[j] = load16<kMfmaKNT>(kb + (kvalid ? koff[j] : kmask[j]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = tc + 4 * c + i < t1 ? voff[i] : vmask;
       if constexpr (VW == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vb + off);
+        const uint4 x = load16<kMfmaVNT>(vb + off);
         r.v[i][0] = x.x;
         r.v[i][1] = x.y;
         r.v[i][2] = x.z;
         r.v[i][3] = x.w;
       } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(vb + off);
+        const uint2 x = load8<kMfmaVNT>(vb + off);
         r.v[i][0] = x.x;
         r.v[i][1] = x.y;
       }
