@@ -343,13 +343,12 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
 // The q.K^T k order is permuted identically in both operands (lane group c,
 // step j covers dims 8c + 32j .. +7), which leaves the dot product unchanged.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 
-constexpr float kLazyMax = 8.0f;
+constexpr float kLazyMax = 8.0f;  // log2 of the largest p allowed before rescaling
 
 // Load flavours of the matrix-core kernel.  Its V loads read whole 256-byte
 // rows per 16 lanes and stream them (non-temporal); its K loads read a 64-byte
@@ -362,7 +361,7 @@ constexpr float kLazyMax = 8.0f;
 #define PKV_MFMA_V_NT 1
 #endif
 constexpr bool kMfmaKNT = PKV_MFMA_K_NT;
-constexpr bool kMfmaVNT = PKV_MFMA_V_NT;  // log2 of the largest p allowed before rescaling
+constexpr bool kMfmaVNT = PKV_MFMA_V_NT;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2v_t v = {lo, hi};
