@@ -245,6 +245,22 @@ pkv_status pkv_append_tokens(pkv_allocator* a, const int64_t* seq_ids,
                              const int32_t* num_tokens, int32_t num_seqs,
                              int64_t* slots_out);
 
+/* Copy-on-write append ("What Is vLLM …", section "How does PagedAttention
+ * work?", memory-sharing step): like pkv_append_tokens, but a sequence whose
+ * last block is partly filled and held by other sequences too (after a full
+ * fork, as beam candidates do) first gets a private copy: a fresh block
+ * replaces it in the sequence's table and the shared block's count drops by
+ * one.  Each copy is reported as a (source, destination) block pair in
+ * copy_pairs_out (host int64 [max_pairs, 2], the pkv_copy_blocks layout) and
+ * *num_pairs_out; the caller copies those blocks (pkv_copy_blocks) before
+ * writing the new tokens.  A full shared block is never copied (the next token
+ * opens a new block).  All-or-nothing: PKV_ERR_OUT_OF_BLOCKS counts the
+ * copies; PKV_ERR_INVALID_ARG if more than max_pairs copies are needed. */
+pkv_status pkv_append_tokens_cow(pkv_allocator* a, const int64_t* seq_ids,
+                                 const int32_t* num_tokens, int32_t num_seqs,
+                                 int64_t* slots_out, int64_t* copy_pairs_out,
+                                 int32_t max_pairs, int32_t* num_pairs_out);
+
 /* Releases the sequence; blocks whose count drops to zero are freed. */
 pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id);
 

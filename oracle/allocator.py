@@ -23,8 +23,12 @@ Readings where the pages are silent (also listed in the design notes):
   source; ``num_tokens`` is a multiple of the block size, or the source's
   whole length (a full fork, as beam candidates do, which may share a
   partly filled last block);
-* appending into a block that more than one sequence holds is refused
-  (copy-on-write is not part of this model);
+* plain appending into a block that more than one sequence holds is refused;
+  the copy-on-write append first gives the writer a private copy of that
+  block (a fresh block from the free list, the shared block's count drops by
+  one) and reports the (source, copy) pair so the caller copies the bytes
+  ("What Is vLLM …", memory-sharing step: sharing by reference counts and
+  copy-on-write);
 * a failing call changes nothing.
 
 Token ``pos`` of a sequence is stored at slot ``table[pos // bs] * bs + pos % bs``.
@@ -137,6 +141,30 @@ class BlockAllocator:
         self.lengths[seq] = length + n
         return slots
 
+    def append_cow(self, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
+        """Grow ``seq`` by ``n`` tokens, copying a shared, partly filled last
+        block first.  Returns (slots, copy pairs (source block, new block))."""
+        if seq not in self.tables:
+            raise NotFound(seq)
+        if n < 0:
+            raise InvalidArg("negative token count")
+        table = self.tables[seq]
+        length = self.lengths[seq]
+        bs = self.block_size
+        copy = n > 0 and length % bs != 0 and self.refcount[table[-1]] > 1
+        need = blocks_for(length + n, bs) - len(table) + (1 if copy else 0)
+        if need > len(self.free):
+            raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
+        pairs = []
+        if copy:
+            old = table[-1]
+            new = self.free.popleft()
+            self.refcount[new] += 1
+            self.refcount[old] -= 1
+            table[-1] = new
+            pairs.append((old, new))
+        return self.append(seq, n), pairs
+
     def fork_prefix(self, src: int, dst: int, num_tokens: int) -> None:
         """Make ``dst`` (empty) share the first ``num_tokens`` tokens of ``src``."""
         if src not in self.tables or dst not in self.tables:
@@ -182,5 +210,7 @@ class BlockAllocator:
                 self.append(op[1], op[2])
             elif op[0] == "fork":
                 self.fork_prefix(op[1], op[2], op[3])
+            elif op[0] == "append_cow":
+                self.append_cow(op[1], op[2])
             else:
                 raise InvalidArg(op)

@@ -59,6 +59,8 @@ EXPORTS = {
     "pkv_seq_fork_prefix": (_i32, [_vp, _i64, _i64, _i32]),
     "pkv_seq_append": (_i32, [_vp, _i64, _i32, _P(_i64)]),
     "pkv_append_tokens": (_i32, [_vp, _P(_i64), _P(_i32), _i32, _P(_i64)]),
+    "pkv_append_tokens_cow": (_i32, [_vp, _P(_i64), _P(_i32), _i32, _P(_i64), _P(_i64), _i32,
+                                     _P(_i32)]),
     "pkv_seq_free": (_i32, [_vp, _i64]),
     "pkv_build_block_tables": (_i32, [_vp, _P(_i64), _i32, _i32, _i32, _P(_i32), _P(_i32)]),
     "pkv_decode_step_prepare": (_i32, [_vp, _P(_i64), _i32, _i32, _i32, _P(_i64), _P(_i32),
@@ -257,6 +259,21 @@ class Allocator:
                                      out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
                "append_tokens")
         return out[:total]
+
+    def append_cow(self, seqs: Sequence[int], counts: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+        """Copy-on-write append: returns (slots, copy pairs int64 [P, 2]); copy
+        the pairs' blocks (``copy_blocks``) before writing the new tokens."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        c = np.ascontiguousarray(counts, dtype=np.int32)
+        slots = np.empty(int(c.sum()) if len(c) else 0, dtype=np.int64)
+        pairs = np.empty((max(len(s), 1), 2), dtype=np.int64)
+        npairs = ctypes.c_int32(0)
+        _check(lib.pkv_append_tokens_cow(self._h, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(s),
+                                         slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         pairs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         len(pairs), ctypes.byref(npairs)), "append_tokens_cow")
+        return slots, pairs[: npairs.value].copy()
 
     def free(self, seq: int) -> None:
         _check(lib.pkv_seq_free(self._h, seq), "seq_free")

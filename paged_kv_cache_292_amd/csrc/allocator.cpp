@@ -161,6 +161,68 @@ extern "C" pkv_status pkv_append_tokens(pkv_allocator* a, const int64_t* seq_ids
   return pkv::ok();
 }
 
+extern "C" pkv_status pkv_append_tokens_cow(pkv_allocator* a, const int64_t* seq_ids,
+                                            const int32_t* num_tokens, int32_t num_seqs,
+                                            int64_t* slots_out, int64_t* copy_pairs_out,
+                                            int32_t max_pairs, int32_t* num_pairs_out) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "append_cow: NULL allocator");
+  if (num_seqs < 0 || max_pairs < 0 || (num_seqs > 0 && (!seq_ids || !num_tokens)) ||
+      (max_pairs > 0 && !copy_pairs_out))
+    return fail(PKV_ERR_INVALID_ARG, "append_cow: bad arguments");
+  // Check everything first, simulating repeated ids in order: a sequence's
+  // shared, partly filled last block is copied once, before its first write.
+  struct Pending {
+    int64_t extra = 0;
+    bool copied = false;
+  };
+  std::unordered_map<int64_t, Pending> pending;
+  int64_t need = 0;
+  int32_t pairs = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PKV_ERR_NOT_FOUND, "append_cow: unknown sequence %lld", (long long)seq_ids[i]);
+    if (num_tokens[i] < 0)
+      return fail(PKV_ERR_INVALID_ARG, "append_cow: negative token count %d", num_tokens[i]);
+    const auto& sq = it->second;
+    Pending& pd = pending[seq_ids[i]];
+    if (pd.extra == 0 && !pd.copied && a->writes_shared(sq, num_tokens[i])) {
+      pd.copied = true;
+      ++need;
+      ++pairs;
+    }
+    const int64_t before = sq.len + pd.extra;
+    need += a->blocks_for(before + num_tokens[i]) - a->blocks_for(before);
+    pd.extra += num_tokens[i];
+  }
+  if (pairs > max_pairs)
+    return fail(PKV_ERR_INVALID_ARG, "append_cow: %d copies needed, room for %d", pairs,
+                max_pairs);
+  if (need > int64_t(a->free_q.size()))
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "append_cow: need %lld blocks, %zu free",
+                (long long)need, a->free_q.size());
+  int32_t np = 0;
+  int64_t* out = slots_out;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto& sq = a->seqs[seq_ids[i]];
+    if (a->writes_shared(sq, num_tokens[i])) {
+      const int32_t old = sq.blocks.back();
+      const int32_t fresh = a->free_q.front();
+      a->free_q.pop_front();
+      a->refcount[size_t(fresh)] += 1;
+      a->refcount[size_t(old)] -= 1;  // still > 0: another sequence holds it
+      sq.blocks.back() = fresh;
+      copy_pairs_out[2 * np] = old;
+      copy_pairs_out[2 * np + 1] = fresh;
+      ++np;
+    }
+    a->grow(sq, num_tokens[i], out);
+    if (out) out += num_tokens[i];
+  }
+  if (num_pairs_out) *num_pairs_out = np;
+  return pkv::ok();
+}
+
 extern "C" pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "seq_free: NULL allocator");
   auto it = a->seqs.find(seq_id);

@@ -61,6 +61,8 @@ _ERR = {OAL.OutOfBlocks: "OUT_OF_BLOCKS", OAL.NotFound: "NOT_FOUND",
 
 def _apply(o, p, op, x, y, k):
     """Run one op on both allocators; results and errors must agree."""
+    if op == "cow":
+        return _apply_cow(o, p, x, k)
     res_o = res_p = None
     err_o = err_p = None
     try:
@@ -80,7 +82,22 @@ def _apply(o, p, op, x, y, k):
         assert list(res_o) == list(res_p)
 
 
-OPS = st.lists(st.tuples(st.sampled_from(["add", "append", "fork", "free"]),
+def _apply_cow(o, p, x, k):
+    err_o = err_p = None
+    try:
+        so, po = o.append_cow(x, k)
+    except OAL.AllocatorError as e:
+        err_o = _ERR[type(e)]
+    try:
+        sp, pp = p.append_cow([x], [k])
+    except P.PkvError as e:
+        err_p = e.code
+    assert err_o == err_p, ("cow", x, k, err_o, err_p)
+    if err_o is None:
+        assert list(so) == list(sp) and [tuple(r) for r in pp] == po
+
+
+OPS = st.lists(st.tuples(st.sampled_from(["add", "append", "fork", "free", "cow"]),
                          st.integers(0, 5), st.integers(0, 5), st.integers(0, 40)),
                max_size=60)
 
@@ -263,3 +280,26 @@ def test_longest_first_order():
     assert P.longest_first_order(np.zeros(0, np.int32)).tolist() == []
     r = W.random_lengths(3, 500, 0, 50).astype(np.int32)
     assert np.array_equal(P.longest_first_order(r), np.argsort(-r, kind="stable"))
+
+
+def test_copy_on_write_batch_matches_oracle():
+    """Batched copy-on-write appends (repeated ids included) equal the oracle's
+    one-by-one appends, slot for slot and pair for pair."""
+    o, p = _both(40, 4, W.permutation(9, 40))
+    for a_ in (o, p):
+        a_.add(0)
+        a_.append(0, 6)
+        a_.add(1)
+        a_.fork_prefix(0, 1, 6)
+        a_.add(2)
+        a_.fork_prefix(0, 2, 6)
+    seqs, counts = [0, 1, 0, 2, 2], [1, 2, 3, 0, 5]
+    ref_slots, ref_pairs = [], []
+    for s_, c_ in zip(seqs, counts):
+        sl, pr = o.append_cow(s_, c_)
+        ref_slots += sl
+        ref_pairs += pr
+    sl, pr = p.append_cow(seqs, counts)
+    assert list(sl) == ref_slots and [tuple(r) for r in pr] == ref_pairs
+    assert len(ref_pairs) == 2  # seq 0 copies, seq 1 copies, seq 2 then holds the block alone
+    _same_state(o, p, range(3), 4)

@@ -138,7 +138,7 @@ def test_build_block_tables():
         a.build_block_tables([7], max_blocks=2)
 
 
-OPS = st.lists(st.tuples(st.sampled_from(["add", "append", "fork", "free"]),
+OPS = st.lists(st.tuples(st.sampled_from(["add", "append", "fork", "free", "cow"]),
                          st.integers(0, 5), st.integers(0, 5), st.integers(0, 40)),
                max_size=60)
 
@@ -160,6 +160,16 @@ def test_invariants_random_ops(ops, bs, n):
                     assert s == t[pos // bs] * bs + pos % bs
             elif op == "fork":
                 a.fork_prefix(x, y, k)
+            elif op == "cow":
+                held = a.table(x)[-1] if x in a.tables and a.tables[x] else None
+                shared = held is not None and a.refcount[held] > 1
+                slots, pairs = a.append_cow(x, k)
+                for src, dst in pairs:
+                    assert src == held and shared and a.refcount[dst] == 1
+                t = a.table(x)
+                for pos, s_ in zip(range(a.context_len(x) - k, a.context_len(x)), slots):
+                    assert s_ == t[pos // bs] * bs + pos % bs
+                    assert a.refcount[t[pos // bs]] == 1  # never written while shared
             else:
                 a.free_seq(x)
         except OAL.AllocatorError:
@@ -200,3 +210,34 @@ def test_workload_replay_shapes():
                 assert a.block_refcount(blk) == s.num_sharers
             for b in wl.sharers:
                 assert a.table(int(b))[: len(pre)] == pre
+
+
+def test_copy_on_write_append():
+    """Beam candidates fork a whole sequence and then diverge: the first writer
+    into the shared, partly filled last block gets a private copy; the last
+    holder writes in place; full shared blocks are never copied."""
+    a = OAL.BlockAllocator(10, 4, free_order=list(range(10)))
+    a.add(0); a.append(0, 6)                  # blocks [0, 1], 2 tokens in block 1
+    a.add(1); a.fork_prefix(0, 1, 6)          # full fork: shares 0 and 1
+    assert a.block_refcount(1) == 2
+    slots, pairs = a.append_cow(0, 3)         # seq 0 copies block 1 -> 2, appends 3 tokens
+    assert pairs == [(1, 2)]
+    assert a.table(0) == [0, 2, 3] and a.table(1) == [0, 1]
+    assert slots == [2 * 4 + 2, 2 * 4 + 3, 3 * 4 + 0]
+    assert a.block_refcount(1) == 1 and a.block_refcount(2) == 1 and a.block_refcount(0) == 2
+    slots, pairs = a.append_cow(1, 1)         # seq 1 now holds block 1 alone: no copy
+    assert pairs == [] and slots == [1 * 4 + 2]
+    # a shared block that is full is not copied: the next token opens a new block
+    a.add(2); a.fork_prefix(1, 2, 4)
+    slots, pairs = a.append_cow(2, 1)
+    assert pairs == [] and a.table(2) == [0, 4] and slots == [16]
+    # zero tokens: nothing copied
+    a.add(3); a.fork_prefix(0, 3, 9)
+    assert a.append_cow(3, 0) == ([], [])
+    # pool exhaustion counts the copy, and leaves everything unchanged
+    free = a.num_free_blocks()
+    snap = (list(a.free), list(a.refcount), {k: list(v) for k, v in a.tables.items()})
+    with pytest.raises(OAL.OutOfBlocks):
+        a.append_cow(3, 3 + 4 * free)
+    assert (list(a.free), list(a.refcount), {k: list(v) for k, v in a.tables.items()}) == snap
+    assert len(a.append_cow(3, 3 + 4 * (free - 1))[1]) == 1

@@ -81,12 +81,17 @@ ALLOC = [
     ("if need > len(self.free):", "if need > len(self.free) + 1:"),
     ("shared = self.tables[src][: blocks_for(num_tokens, bs)]", "shared = self.tables[src][: num_tokens // bs]"),
     ("tables[i, : len(t)] = t", "tables[i, : len(t)] = t[::-1]"),
+    ("copy = n > 0 and length % bs != 0 and self.refcount[table[-1]] > 1",
+     "copy = n > 0 and self.refcount[table[-1]] > 1"),
+    ("            self.refcount[old] -= 1\n", "\n"),
+    ("- len(table) + (1 if copy else 0)", "- len(table)"),
 ]
 
 ALLOC_PINS = ["test_worked_example_960_vs_16384", "test_block_lookup_example",
               "test_fifo_policy_and_free_order", "test_errors_leave_state_unchanged",
               "test_shared_write_refused", "test_build_block_tables",
-              "test_invariants_random_ops", "test_workload_replay_shapes"]
+              "test_invariants_random_ops", "test_workload_replay_shapes",
+              "test_copy_on_write_append"]
 
 
 @pytest.mark.parametrize("old,new", ALLOC, ids=[f"alloc{i}" for i in range(len(ALLOC))])
