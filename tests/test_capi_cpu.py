@@ -303,3 +303,10 @@ def test_copy_on_write_batch_matches_oracle():
     assert list(sl) == ref_slots and [tuple(r) for r in pr] == ref_pairs
     assert len(ref_pairs) == 2  # seq 0 copies, seq 1 copies, seq 2 then holds the block alone
     _same_state(o, p, range(3), 4)
+
+
+def test_decode_rejects_too_many_partitions():
+    """A partition grid beyond 65,535 columns is refused before any launch."""
+    st = _decode(part=16, max_ctx=16 * 70000, max_blocks=70000, q=1, k=1, v=1, tables=1, ctx=1,
+                 out=1, ws=1, ws_bytes=1 << 62)
+    assert st == -1 and "partitions" in P.lib.pkv_last_error().decode()

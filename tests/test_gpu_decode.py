@@ -170,3 +170,20 @@ def test_launch_order_does_not_change_results(cfg, decode_path):
                 got = run_decode(st, part, order)
                 np.testing.assert_array_equal(got, base)
             assert_close(base, ref, s.dtype, f"{s.name} order p{part} path{path}")
+
+
+def test_maximum_batch_and_context():
+    """The largest batch the grid takes (65,535 sequences of 1..4 tokens) and a
+    single 131,089-token context (8,194 blocks): sampled rows vs the oracle."""
+    s = W.DecodeShape("max_batch", "bf16", 65535, 2, 1, 64, 16, "uniform", ctx_lo=1, ctx_hi=4,
+                      seed=91)
+    st = build_step(s, poison=True)
+    got = run_decode(st, P.PARTITION_AUTO)
+    pairs = [(b, h) for b in (0, 1, 4095, 40000, 65534) for h in (0, 1)]
+    assert_close(np.stack([got[b, h] for b, h in pairs]), oracle_rows(st, pairs), "bf16",
+                 "65535 sequences")
+    s2 = W.DecodeShape("max_ctx", "bf16", 2, 8, 1, 128, 16, "fixed", ctx_fixed=(131089, 3), seed=92)
+    st2 = build_step(s2, poison=True)
+    ref = oracle_full(st2)
+    for part in (0, 16, P.PARTITION_AUTO):
+        assert_close(run_decode(st2, part), ref, "bf16", f"131089 tokens p{part}")
