@@ -158,16 +158,20 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   for (int i = 0; i < 4; ++i)
     slot_off[i] = uint32_t(((4 * i + grp) * row_stride + r * EPL) * int(sizeof(T)));
   const uint32_t lane_off = uint32_t(r * EPL * int(sizeof(T)));
-  auto load_chunk = [&](int c, F (&kd)[4], F (&vd)[4]) {
+  // `live` false: the prefetch past a wave's last chunk, which only keeps the
+  // loop free of branches; every lane then reads the cache's first 16 bytes
+  // (one line per wave instead of re-reading a whole chunk from HBM).
+  auto load_chunk = [&](int c, F (&kd)[4], F (&vd)[4], bool live) {
     const int tc = __builtin_amdgcn_readfirstlane(c * kChunk);  // wave-uniform: scalar loads
     int bid = scalar_read(tbl + tc / BS);
     bid = (unsigned)bid < (unsigned)a.num_blocks ? bid : 0;
-    const size_t rowbase = ((size_t(bid) * BS + (tc % BS)) * row_stride + kvh * D) * sizeof(T);
+    const size_t rowbase =
+        live ? ((size_t(bid) * BS + (tc % BS)) * row_stride + kvh * D) * sizeof(T) : 0;
     const char* kb = reinterpret_cast<const char*>(kc) + rowbase;
     const char* vb = reinterpret_cast<const char*>(vc) + rowbase;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = tc + 4 * i + grp < t1 ? slot_off[i] : lane_off;
+      const uint32_t off = !live ? 0u : (tc + 4 * i + grp < t1 ? slot_off[i] : lane_off);
       load_frag_stream(kd[i], kb + off);
       load_frag_stream(vd[i], vb + off);
     }
@@ -221,21 +225,20 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     }
   };
 
-  // Two register buffers, alternating; the prefetch past the last chunk
-  // re-reads the current chunk (a cache hit) so that it needs no branch.
+  // Two register buffers, alternating.
   F ka[4], va[4], kb2[4], vb2[4];
   int c = c_begin + wave;
   if (c < c_end) {
-    load_chunk(c, ka, va);
+    load_chunk(c, ka, va, true);
     while (true) {
-      int cn = c + NW < c_end ? c + NW : c;
-      load_chunk(cn, kb2, vb2);
+      bool live = c + NW < c_end;
+      load_chunk(live ? c + NW : c, kb2, vb2, live);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
       consume(c, ka, va);
       c += NW;
       if (c >= c_end) break;
-      cn = c + NW < c_end ? c + NW : c;
-      load_chunk(cn, ka, va);
+      live = c + NW < c_end;
+      load_chunk(live ? c + NW : c, ka, va, live);
       __builtin_amdgcn_sched_barrier(0);
       consume(c, kb2, vb2);
       c += NW;
@@ -436,20 +439,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     uint4 k[KSTEPS];
     uint32_t v[4][VW];
   };
-  auto load_chunk = [&](int ch, Regs& r) {
+  // `live` false: the branch-free prefetch past a wave's last chunk; every
+  // lane then reads the cache's first 16 bytes.
+  auto load_chunk = [&](int ch, Regs& r, bool live) {
     const int tc = __builtin_amdgcn_readfirstlane(ch * kChunk);
     int bid = scalar_read(tbl + tc / BS);
     bid = (unsigned)bid < (unsigned)a.num_blocks ? bid : 0;
-    const size_t rowbase = ((size_t(bid) * BS + (tc % BS)) * row_stride + size_t(kvh) * D) * 2;
+    const size_t rowbase =
+        live ? ((size_t(bid) * BS + (tc % BS)) * row_stride + size_t(kvh) * D) * 2 : 0;
     const char* kb = kc + rowbase;
     const char* vb = vc + rowbase;
     const bool kvalid = tc + n < t1;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j)
-      r.k[j] = load16<kMfmaKNT>(kb + (kvalid ? koff[j] : kmask[j]));
+      r.k[j] = load16<kMfmaKNT>(kb + (!live ? 0u : (kvalid ? koff[j] : kmask[j])));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = tc + 4 * c + i < t1 ? voff[i] : vmask;
+      const uint32_t off = !live ? 0u : (tc + 4 * c + i < t1 ? voff[i] : vmask);
       if constexpr (VW == 4) {
         const uint4 x = load16<kMfmaVNT>(vb + off);
         r.v[i][0] = x.x;
@@ -512,16 +518,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   Regs ra, rb;
   int ch = c_begin + wave;
   if (ch < c_end) {
-    load_chunk(ch, ra);
+    load_chunk(ch, ra, true);
     while (true) {
-      int cn = ch + NW < c_end ? ch + NW : ch;
-      load_chunk(cn, rb);
+      bool live = ch + NW < c_end;
+      load_chunk(live ? ch + NW : ch, rb, live);
       __builtin_amdgcn_sched_barrier(0);
       consume(ch, ra);
       ch += NW;
       if (ch >= c_end) break;
-      cn = ch + NW < c_end ? ch + NW : ch;
-      load_chunk(cn, ra);
+      live = ch + NW < c_end;
+      load_chunk(live ? ch + NW : ch, ra, live);
       __builtin_amdgcn_sched_barrier(0);
       consume(ch, rb);
       ch += NW;
