@@ -25,7 +25,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["widen", "gather_sequence", "attend", "paged_decode", "paged_decode_one",
-           "softmax_weights"]
+           "softmax_weights", "paged_prefill"]
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -100,4 +100,42 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
         for h in range(Hq):
             g = h // group
             out[b, h] = attend(qf[b, h], k[:, g, :], v[:, g, :], scale)
+    return out
+
+
+def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+                  dtype: str = "f32") -> np.ndarray:
+    """Several new tokens per sequence (a prompt chunk) attend to the paged cache.
+
+    Long prompts are processed in pieces so one large prefill does not stall
+    the decoding sequences ("Serving models with vLLM", section "How it works:
+    continuous batching", chunked prefill).  Sequence ``b`` owns query rows
+    ``query_start[b] .. query_start[b+1]-1`` of ``q [T, Hq, D]``; its chunk of
+    ``n_b`` tokens is the end of its context (their K/V already in the cache),
+    so query ``i`` sits at position ``ctx_b - n_b + i`` and, like any token,
+    attends to every earlier token and itself ("vLLM in Production …",
+    section "The KV Cache and the 60–80% Memory Tax") — positions ``0 ..
+    ctx_b - n_b + i``.  A query whose position is negative (a chunk longer
+    than its context) gets zeros.  Returns float64 ``[T, Hq, D]``."""
+    qf = widen(q, dtype)
+    T, Hq, D = qf.shape
+    Hkv = k_cache.shape[2]
+    bs = k_cache.shape[1]
+    group = Hq // Hkv
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for b in range(len(context_lens)):
+        ctx = int(context_lens[b])
+        lo, hi = int(query_start[b]), int(query_start[b + 1])
+        n = hi - lo
+        if ctx == 0 or n == 0:
+            continue
+        k = widen(gather_sequence(k_cache, block_tables[b], ctx, bs), dtype)
+        v = widen(gather_sequence(v_cache, block_tables[b], ctx, bs), dtype)
+        for i in range(n):
+            pos = ctx - n + i
+            if pos < 0:
+                continue
+            for h in range(Hq):
+                g = h // group
+                out[lo + i, h] = attend(qf[lo + i, h], k[: pos + 1, g, :], v[: pos + 1, g, :], scale)
     return out

@@ -187,8 +187,59 @@ def pin_one(mod):
     assert (mod.attend(q[0, 0], np.zeros((0, D)), np.zeros((0, D)), 0.3) == 0).all()
 
 
+def _brute_causal(q_rows, contig_k, contig_v, ctxs, starts, scale, group):
+    """Loops with math.exp; query i of sequence b sees tokens 0..ctx-n+i."""
+    T, Hq, D = q_rows.shape
+    out = np.zeros((T, Hq, D))
+    for b, c in enumerate(ctxs):
+        lo, hi = starts[b], starts[b + 1]
+        n = hi - lo
+        for i in range(n):
+            pos = c - n + i
+            if pos < 0:
+                continue
+            for h in range(Hq):
+                g = h // group
+                e = [math.exp(scale * sum(q_rows[lo + i, h, d] * contig_k[b][t, g, d] for d in range(D)))
+                     for t in range(pos + 1)]
+                z = sum(e)
+                for d in range(D):
+                    out[lo + i, h, d] = sum(e[t] * contig_v[b][t, g, d] for t in range(pos + 1)) / z
+    return out
+
+
+def pin_prefill(mod):
+    """Chunked prefill: brute-force causal loops, torch SDPA with an explicit
+    bottom-right causal mask, and the one-query case equal to decode."""
+    ctxs, Hq, Hkv, D, bs = [9, 20, 4, 17], 4, 2, 4, 8
+    chunks = [3, 20, 6, 1]          # the third chunk is longer than its context
+    starts = np.concatenate([[0], np.cumsum(chunks)])
+    q = _rand(61, int(starts[-1]), Hq, D)
+    _, ck, cv = _case(62, ctxs, Hq, Hkv, D, bs)
+    kc, vc, tb = _page(ck, cv, ctxs, bs, perm_seed=8)
+    got = mod.paged_prefill(q, kc, vc, tb, np.array(ctxs), starts, 0.41, "f32")
+    ref = _brute_causal(q, ck, cv, ctxs, starts, 0.41, Hq // Hkv)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    assert (got[starts[2]:starts[2] + 2] == 0).all()  # positions -2, -1
+    b = 1
+    qt = torch.from_numpy(q[starts[b]:starts[b + 1]]).permute(1, 0, 2)              # [Hq, n, D]
+    kt = torch.from_numpy(ck[b]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)  # [Hq, T, D]
+    vt = torch.from_numpy(cv[b]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    n, T = chunks[b], ctxs[b]
+    mask = torch.tensor([[t <= T - n + i for t in range(T)] for i in range(n)])
+    sd = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.41)
+    np.testing.assert_allclose(got[starts[b]:starts[b + 1]], sd.permute(1, 0, 2).numpy(),
+                               rtol=1e-12, atol=1e-13)
+    # one query per sequence is the decode step
+    ones = np.arange(len(ctxs) + 1)
+    q1 = _rand(63, len(ctxs), Hq, D)
+    np.testing.assert_allclose(mod.paged_prefill(q1, kc, vc, tb, np.array(ctxs), ones, 0.41, "f32"),
+                               mod.paged_decode(q1, kc, vc, tb, np.array(ctxs), 0.41, "f32"),
+                               rtol=1e-15, atol=0)
+
+
 PINS = [pin_brute_force, pin_torch_sdpa, pin_closed_forms, pin_widen,
-        pin_placement_and_sharing, pin_unused_slots_and_padding, pin_one]
+        pin_placement_and_sharing, pin_unused_slots_and_padding, pin_one, pin_prefill]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])

@@ -48,6 +48,10 @@ ATTN = [
     ("z = logits - logits.max(axis=-1, keepdims=True)", "z = logits - logits.max(axis=-1, keepdims=True) * 0 + 1e-3 * logits"),
     ("return np.zeros(q_bh.shape[-1], dtype=np.float64)", "return np.ones(q_bh.shape[-1], dtype=np.float64)"),
     ("np.asarray(x, dtype=np.float32).astype(np.float64)", "np.asarray(x, dtype=np.float16).astype(np.float64)"),
+    ("pos = ctx - n + i", "pos = ctx - n + i - 1"),
+    ("k[: pos + 1, g, :], v[: pos + 1, g, :]", "k[:ctx, g, :], v[:ctx, g, :]"),
+    ("out[lo + i, h] = attend(qf[lo + i, h]", "out[lo + i, h] = attend(qf[lo, h]"),
+    ("            if pos < 0:\n                continue\n", "\n"),
 ]
 
 
