@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 
 
 def _args():
@@ -36,7 +37,8 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--shape", type=int, default=2, help="decode shape index 0..4 (default 2)")
+    ap.add_argument("--shape", type=int, default=2,
+                    help="decode shape index 0..4 (default 2), or 5 for the chunked-prefill step")
     ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 single pass, else tokens")
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto",
                     help="decode kernel: automatic choice, vector ALUs or matrix cores")
@@ -219,7 +221,9 @@ def main() -> int:
     s = W.shape(args.shape)
     total_steps = args.warmup + args.steps
     step_new = 1 if s.new_tokens else 0
-    wl = W.make_workload(s, extra_tokens=total_steps * step_new)
+    chunk = s.chunk  # > 0: a chunked-prefill step of this many tokens per sequence
+    step_tok = chunk if chunk else step_new  # tokens each sequence gains per step
+    wl = W.make_workload(s, extra_tokens=total_steps * step_tok)
     B, Hq, Hkv, D, bs = s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size
     dt_code = P.F32 if s.dtype == "f32" else P.BF16
     tdt = torch.float32 if s.dtype == "f32" else torch.bfloat16
@@ -232,16 +236,17 @@ def main() -> int:
     alloc = P.Allocator(wl.num_blocks, bs, wl.free_order)
     alloc.replay(wl.ops)
     seqs = np.arange(B, dtype=np.int64)
-    final_ctx = wl.ctx + (total_steps - 1) * step_new
+    final_ctx = wl.ctx + (total_steps - 1) * step_tok
     max_blocks = int(((final_ctx + bs - 1) // bs).max())
     max_ctx_final = int(final_ctx.max())
 
     q = up(wl.q)
     k_cache = up(wl.k_cache)
     v_cache = up(wl.v_cache)
-    out = torch.empty((B, Hq, D), dtype=tdt, device=dev)
+    rows = B * chunk if chunk else B  # query rows per step
+    out = torch.empty((rows, Hq, D), dtype=tdt, device=dev)
     new_k = new_v = None
-    if step_new:
+    if step_tok:
         nks, nvs = [wl.new_k], [wl.new_v]
         for i in range(1, total_steps):
             k_, v_ = W.step_tokens(s, i)
@@ -249,15 +254,23 @@ def main() -> int:
             nvs.append(v_)
         new_k = up(np.stack(nks))
         new_v = up(np.stack(nvs))
-    ws_bytes = P.decode_workspace_bytes(B, Hq, Hkv, D, bs, max_ctx_final, args.partition, dt_code)
+    if chunk:
+        ws_bytes = P.prefill_workspace_bytes(rows, Hq, D, max_ctx_final, args.partition)
+        d_qstart = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * chunk).to(dev)
+        chunk_counts = np.full(B, chunk, dtype=np.int32)
+    else:
+        ws_bytes = P.decode_workspace_bytes(B, Hq, Hkv, D, bs, max_ctx_final, args.partition,
+                                            dt_code)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    part_used = P.decode_partition_size(B, Hq, Hkv, D, bs, max_ctx_final, args.partition, dt_code)
+    part_used = (P.prefill_partition_size(B, chunk, Hq, Hkv, max_ctx_final, args.partition)
+                 if chunk else
+                 P.decode_partition_size(B, Hq, Hkv, D, bs, max_ctx_final, args.partition, dt_code))
 
     # One pinned staging buffer per in-flight step, laid out as the device
     # buffer it is copied to: slots int64 [B] | tables int32 [B, max_blocks] |
     # context lengths int32 [B].  One H2D copy per step.
     nbuf = args.staging_depth  # the host waits only for copies this many steps back
-    n_slot_b, n_tab_b, n_ctx_b, n_ord_b = 8 * B, 4 * B * max_blocks, 4 * B, 4 * B
+    n_slot_b, n_tab_b, n_ctx_b, n_ord_b = 8 * B * max(step_tok, 1), 4 * B * max_blocks, 4 * B, 4 * B
     stage_bytes = n_slot_b + n_tab_b + n_ctx_b + n_ord_b
     stage_bytes = (stage_bytes + 15) // 16 * 16
     h_stage = [torch.empty(stage_bytes, dtype=torch.uint8).pin_memory() for _ in range(nbuf)]
@@ -276,8 +289,8 @@ def main() -> int:
     use_order = args.order == "longest"
     copied = [torch.cuda.Event() for _ in range(nbuf)]
     stream = torch.cuda.current_stream()
-    new_k_steps = [new_k[i] for i in range(total_steps)] if step_new else None
-    new_v_steps = [new_v[i] for i in range(total_steps)] if step_new else None
+    new_k_steps = [new_k[i] for i in range(total_steps)] if step_tok else None
+    new_v_steps = [new_v[i] for i in range(total_steps)] if step_tok else None
 
     # per-step algorithmic bytes of the decode call
     E = s.elem_bytes
@@ -309,7 +322,13 @@ def main() -> int:
         # copy then moves the step's slots, tables and lengths into the pinned
         # staging buffer, which is uncached and never read back by the host.
         cx = np.empty(B, np.int32)
-        if step_new:
+        if chunk:
+            alloc.append_tokens(seqs, chunk_counts, out=host_sl)
+            alloc.build_block_tables(seqs, max_blocks, pad=-1, tables_out=host_tb, ctx_out=cx)
+            maxc = int(cx.max())
+            if use_order:
+                host_ord[:] = P.longest_first_order(cx)
+        elif step_new:
             maxc = alloc.decode_step_prepare(seqs, max_blocks, host_sl, host_tb, cx,
                                              order_out=host_ord if use_order else None)
         else:
@@ -321,12 +340,17 @@ def main() -> int:
         np.copyto(h_flat[j], host_flat)
         P.upload_pinned(d_stage, h_stage[j])
         copied[j].record(stream)
-        if step_new:
+        if step_tok:
             P.kv_reshape_and_cache(new_k_steps[i], new_v_steps[i], k_cache, v_cache, d_slots)
         ev[i][0].record(stream)
-        P.paged_attention_decode(out, q, k_cache, v_cache, d_tables, d_ctx, maxc, s.scale,
-                                 args.partition, workspace,
-                                 seq_order=d_order if use_order else None)
+        if chunk:
+            P.paged_attention_prefill(out, q, d_qstart, chunk, k_cache, v_cache, d_tables, d_ctx,
+                                      maxc, s.scale, args.partition, workspace,
+                                      seq_order=d_order if use_order else None)
+        else:
+            P.paged_attention_decode(out, q, k_cache, v_cache, d_tables, d_ctx, maxc, s.scale,
+                                     args.partition, workspace,
+                                     seq_order=d_order if use_order else None)
         ev[i][1].record(stream)
         ctx_hist.append(cx)
         host_s.append(time.perf_counter() - t_h)
@@ -374,7 +398,7 @@ def main() -> int:
         "config": {
             "workload": s.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": bs, "mean_context": round(tok_t / K / B, 1),
-            "max_context": max_ctx_final, "new_tokens_per_step": B * step_new,
+            "max_context": max_ctx_final, "new_tokens_per_step": B * step_tok,
             "partition_size": part_used, "kv_bytes_per_step": int(kv_t // K),
             "decode_path": args.path, "launch_order": args.order,
         },
@@ -386,6 +410,22 @@ def main() -> int:
             "algorithmic_bytes_per_launch": int(alg_per_launch),
         },
     }
+    if chunk:
+        # prefill: attention flops (q.K and P.V, 2 flops per multiply-add) over
+        # each query's visible tokens; a dense bf16 contraction on the matrix cores
+        def flops(ctx):
+            pos_sum = sum(int(c) * chunk - chunk * (chunk - 1) // 2 for c in ctx)
+            return 4 * D * Hq * pos_sum
+        fl = float(np.mean([flops(c) for c in ctx_hist[timed]]))
+        tflops = fl / dec_avg_s / 1e12
+        res["roofline"] = {
+            "kernel": "paged_attention_prefill (matrix-core partition kernel + merge)",
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "avg_launch_us": round(dec_avg_s * 1e6, 2), "flops_per_launch": int(fl),
+            "kv_GBps_unique": round(achieved, 1),
+        }
+        res["prefill_tokens_per_s"] = round(rows * K / elapsed, 1)
     tr = load_traffic(s.name, args.path)
     if tr is not None and tr["steps"] == args.steps and tr["warmup"] == args.warmup:
         res["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]

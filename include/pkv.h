@@ -177,6 +177,59 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q,
                                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * Chunked prefill: several new tokens per sequence attend to the paged cache
+ * (long prompts are processed in pieces so that one large prefill does not
+ * stall decoding: "Serving models with vLLM", section "How it works:
+ * continuous batching").  Sequence b owns query rows query_start[b] ..
+ * query_start[b+1]-1 of q and out; its n_b new tokens are the last n_b of its
+ * context (their K/V already written, e.g. by pkv_kv_reshape_and_cache), so
+ * query i sits at position context_lens[b] - n_b + i and attends to tokens
+ * 0 .. that position (causal).  A query with a negative position (a chunk
+ * longer than its context) gets zeros; a sequence with no queries is
+ * skipped.  n_b = 1 for every sequence is the decode step.
+ *
+ * out, q        device, [total_queries, num_q_heads, head_dim] (bf16).
+ * query_start   device, int32 [num_seqs + 1], non-decreasing, last entry
+ *               total_queries (entries are clamped into [0, total_queries]).
+ * max_queries_per_seq  host-side upper bound of n_b (sizes the grid; rows
+ *               past it are not computed).
+ * Other arguments as pkv_paged_attention_decode; the workspace size is
+ * pkv_prefill_workspace_bytes(...) (for AUTO it covers the partitioned
+ * case; pkv_prefill_partition_size tells what AUTO resolves to: single pass
+ * unless the query tiles give fewer than about four workgroups per CU).  Runs on the matrix cores: each tile holds
+ * 16 (query, head) rows — floor(16 / G) queries of one sequence times the G
+ * query heads of one kv head — and the tiles of a workgroup share each K/V
+ * chunk through LDS.  bf16 only; head_dim in {64, 128};
+ * block_size in {16, 32}; G = num_q_heads / num_kv_heads in 1..16.
+ * ---------------------------------------------------------------------- */
+size_t pkv_prefill_workspace_bytes(int32_t total_queries, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t partition_size);
+
+/* The partition size a prefill call with these arguments uses (resolves
+ * AUTO); 0 means single pass. */
+int32_t pkv_prefill_partition_size(int32_t num_seqs, int32_t max_queries_per_seq,
+                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t max_context_len, int32_t partition_size);
+
+pkv_status pkv_paged_attention_prefill(void* out, const void* q,
+                                       const int32_t* query_start,
+                                       int32_t total_queries,
+                                       int32_t max_queries_per_seq,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens,
+                                       const int32_t* seq_order,
+                                       int32_t max_context_len, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, float scale,
+                                       int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes, pkv_dtype dtype,
+                                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Block copy: cache[dst] = cache[src] for each (src, dst) pair, K and V.
  * Used to give a sequence a private copy of a block that others still hold
  * (copy-on-write of a shared block, "What Is vLLM …", section "How does

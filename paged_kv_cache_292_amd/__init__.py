@@ -19,6 +19,7 @@ __all__ = [
     "LIB_PATH", "lib", "PkvError", "F32", "BF16", "PARTITION_AUTO",
     "kv_reshape_and_cache", "paged_attention_decode", "decode_workspace_bytes",
     "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned", "longest_first_order",
+    "paged_attention_prefill", "prefill_workspace_bytes", "prefill_partition_size",
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
 ]
 
@@ -49,6 +50,11 @@ EXPORTS = {
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                           _i32, _vp]),
     "pkv_longest_first_order": (_i32, [_P(_i32), _i32, _P(_i32)]),
+    "pkv_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_prefill_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _vp,
+                                           _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                           _i32, _vp, _sz, _i32, _vp]),
     "pkv_set_decode_path": (_i32, [_i32]),
     "pkv_get_decode_path": (_i32, []),
     "pkv_upload_pinned": (_i32, [_vp, _vp, _sz, _vp]),
@@ -196,6 +202,39 @@ def set_decode_path(path: int) -> None:
 
 def get_decode_path() -> int:
     return int(lib.pkv_get_decode_path())
+
+
+def prefill_workspace_bytes(total_queries, num_q_heads, head_dim, max_context_len,
+                            partition_size=PARTITION_AUTO) -> int:
+    return int(lib.pkv_prefill_workspace_bytes(total_queries, num_q_heads, head_dim,
+                                               max_context_len, partition_size))
+
+
+def prefill_partition_size(num_seqs, max_queries_per_seq, num_q_heads, num_kv_heads,
+                           max_context_len, partition_size=PARTITION_AUTO) -> int:
+    """Partition size a prefill call uses (AUTO resolved); 0 = single pass."""
+    return int(lib.pkv_prefill_partition_size(num_seqs, max_queries_per_seq, num_q_heads,
+                                              num_kv_heads, max_context_len, partition_size))
+
+
+def paged_attention_prefill(out, q, query_start, max_queries_per_seq: int, k_cache, v_cache,
+                            block_tables, context_lens, max_context_len: int, scale: float,
+                            partition_size: int = PARTITION_AUTO, workspace=None, stream=None,
+                            seq_order=None) -> None:
+    """Chunked prefill: query rows ``query_start[b] .. query_start[b+1]-1`` of
+    ``q [T, Hq, D]`` are the last tokens of sequence ``b`` and attend causally
+    to its paged context.  ``query_start``: device int32 ``[B + 1]``."""
+    N, bs, Hkv, D = k_cache.shape
+    T, Hq, _ = q.shape
+    B = context_lens.shape[0]
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_prefill(
+        out.data_ptr(), q.data_ptr(), query_start.data_ptr(), T, int(max_queries_per_seq),
+        k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), seq_order.data_ptr() if seq_order is not None else None,
+        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size), ws_ptr,
+        ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_prefill")
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:

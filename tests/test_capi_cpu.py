@@ -221,6 +221,17 @@ def test_decode_workspace_and_partition_queries():
     assert _decode(part=16, q=1, k=1, v=1, tables=1, ctx=1, out=1) == -6
 
 
+def test_prefill_partition_query():
+    """AUTO prefill runs single pass when the query tiles fill the grid (16
+    sequences x 40 heads x 512-token chunks) and partitions a small grid; an
+    explicit size passes through."""
+    assert P.prefill_partition_size(16, 512, 40, 40, 4096) == 0
+    assert P.prefill_partition_size(1, 16, 8, 8, 32768) == 2048
+    assert P.prefill_partition_size(1, 16, 8, 8, 1000) == 0  # short context: one pass anyway
+    assert P.prefill_partition_size(16, 512, 40, 40, 4096, 256) == 256
+    assert P.prefill_partition_size(16, 512, 40, 40, 4096, 0) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(D=80), -2), (dict(T=-1), -1), (dict(kstride=100), -1), (dict(dtype=3), -1),
 ])

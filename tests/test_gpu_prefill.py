@@ -1,0 +1,144 @@
+"""GPU parity of chunked prefill (several new tokens per sequence, causal)
+against the fp64 oracle, following the serving flow: the allocator appends
+each sequence's chunk, the cache write stores the chunk's K/V, then prefill
+runs over the chunk's queries."""
+import numpy as np
+import pytest
+
+import oracle.allocator as OAL
+import oracle.attention as OA
+import oracle.cache_write as OC
+import workloads as W
+from gpu_cases import assert_close, from_dev, log, poison_unused_tail, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+import paged_kv_cache_292_amd as P  # noqa: E402
+
+
+def _prefill_case(prior, chunks, Hq, Hkv, D, bs, seed):
+    """Caches holding each sequence's prior context, then its chunk appended
+    and written.  Returns host (oracle) and device views."""
+    B = len(prior)
+    total_ctx = [p + c for p, c in zip(prior, chunks)]
+    N = sum(-(-t // bs) for t in total_ctx) + 3
+    n = N * bs * Hkv * D
+    kc = W.normal_bf16_bits(seed, 1, n).reshape(N, bs, Hkv, D)
+    vc = W.normal_bf16_bits(seed, 2, n).reshape(N, bs, Hkv, D)
+    fo = W.permutation(seed, N)
+    o = OAL.BlockAllocator(N, bs, fo)
+    p = P.Allocator(N, bs, fo)
+    for a in (o, p):
+        for b in range(B):
+            a.add(b)
+            if prior[b]:
+                a.append(b, prior[b])
+    slots_o = [s for b in range(B) for s in o.append(b, chunks[b])]
+    slots_p = p.append_tokens(list(range(B)), chunks)
+    assert list(slots_p) == slots_o
+    mb = max(-(-t // bs) for t in total_ctx) + 1
+    tables, ctx = o.build_block_tables(list(range(B)), mb)
+    tp, cp = p.build_block_tables(list(range(B)), mb)
+    assert np.array_equal(tables, tp) and np.array_equal(ctx, cp)
+    T = sum(chunks)
+    new_k = W.normal_bf16_bits(seed, 3, T * Hkv * D).reshape(T, Hkv, D)
+    new_v = W.normal_bf16_bits(seed, 4, T * Hkv * D).reshape(T, Hkv, D)
+    poison_unused_tail(kc, tables, ctx, "bf16")
+    poison_unused_tail(vc, tables, ctx, "bf16")
+    kd, vd = to_dev(kc, "bf16"), to_dev(vc, "bf16")
+    if T:
+        P.kv_reshape_and_cache(to_dev(new_k, "bf16"), to_dev(new_v, "bf16"), kd, vd,
+                               torch.from_numpy(np.asarray(slots_p, np.int64)).cuda())
+    ko, vo = OC.reshape_and_cache(new_k, new_v, kc, vc, slots_o)
+    q = W.normal_bf16_bits(seed, 5, max(T, 1) * Hq * D).reshape(max(T, 1), Hq, D)[:T]
+    starts = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    return dict(q=q, ko=ko, vo=vo, tables=tables, ctx=ctx, starts=starts, kd=kd, vd=vd,
+                tp=torch.from_numpy(tp).cuda(), cp=torch.from_numpy(cp).cuda(),
+                sd=torch.from_numpy(starts).cuda(), max_q=max(chunks), max_ctx=int(ctx.max()))
+
+
+def _run(cs, Hq, D, part, scale, ctx_dev=None, order=None):
+    T = cs["q"].shape[0]
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    wsb = P.prefill_workspace_bytes(T, Hq, D, cs["max_ctx"], part)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None
+    so = torch.from_numpy(order).cuda() if order is not None else None
+    P.paged_attention_prefill(out, to_dev(cs["q"], "bf16"), cs["sd"], cs["max_q"], cs["kd"],
+                              cs["vd"], cs["tp"], cs["cp"] if ctx_dev is None else ctx_dev,
+                              cs["max_ctx"], scale, part, ws, seq_order=so)
+    torch.cuda.synchronize()
+    return OA.widen(from_dev(out, "bf16"), "bf16")
+
+
+CASES = [
+    # prior context, chunk sizes, Hq, Hkv, D, bs
+    ((0, 50, 1000, 5, 3000, 40), (1, 7, 16, 33, 100, 0), 4, 4, 128, 16),
+    ((200, 0, 4000), (17, 64, 3), 8, 2, 128, 32),
+    ((700, 31, 2100), (40, 9, 129), 16, 2, 64, 16),
+    ((90, 2500), (11, 23), 10, 2, 128, 16),
+    ((333, 1), (5, 70), 32, 2, 128, 32),
+    ((5000,), (300,), 8, 8, 128, 16),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("part", [0, 64, P.PARTITION_AUTO])
+def test_chunked_prefill_matches_oracle(case, part):
+    prior, chunks, Hq, Hkv, D, bs = CASES[case]
+    log(f"prefill case {case} G={Hq // Hkv} D={D} bs={bs} chunks={chunks} partition={part}")
+    cs = _prefill_case(prior, chunks, Hq, Hkv, D, bs, seed=300 + case)
+    scale = 1.0 / np.sqrt(D)
+    got = _run(cs, Hq, D, part, scale)
+    ref = OA.paged_prefill(cs["q"], cs["ko"], cs["vo"], cs["tables"], cs["ctx"], cs["starts"],
+                           scale, "bf16")
+    assert_close(got, ref, "bf16", f"prefill case {case} p{part}")
+    order = P.longest_first_order(cs["ctx"])
+    np.testing.assert_array_equal(_run(cs, Hq, D, part, scale, order=order), got)
+
+
+def test_prefill_queries_before_the_context_start_get_zeros():
+    """A chunk longer than its sequence's context length (by the context
+    lengths passed in) leaves the queries at negative positions at zero."""
+    cs = _prefill_case((10, 40), (8, 6), 4, 2, 128, 16, seed=350)
+    short = cs["ctx"].copy()
+    short[0] = 5  # 8 queries, context 5: the first three sit before position 0
+    got = _run(cs, 4, 128, 0, 0.1, ctx_dev=torch.from_numpy(short).cuda())
+    ref = OA.paged_prefill(cs["q"], cs["ko"], cs["vo"], cs["tables"], short, cs["starts"], 0.1,
+                           "bf16")
+    assert (got[:3] == 0).all()
+    assert_close(got, ref, "bf16", "negative positions")
+
+
+def test_prefill_of_one_token_is_decode():
+    """One query per sequence through prefill equals the decode kernel (up to
+    one bf16 rounding step: the two sum the tokens in different orders)."""
+    cs = _prefill_case((100, 2000, 17), (1, 1, 1), 16, 4, 128, 32, seed=360)
+    got = _run(cs, 16, 128, P.PARTITION_AUTO, 0.09)
+    out = torch.empty((3, 16, 128), dtype=torch.bfloat16, device="cuda")
+    wsb = P.decode_workspace_bytes(3, 16, 4, 128, 32, cs["max_ctx"], P.PARTITION_AUTO)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    P.paged_attention_decode(out, to_dev(cs["q"], "bf16"), cs["kd"], cs["vd"], cs["tp"],
+                             cs["cp"], cs["max_ctx"], 0.09, P.PARTITION_AUTO, ws)
+    torch.cuda.synchronize()
+    dec = OA.widen(from_dev(out, "bf16"), "bf16")
+    np.testing.assert_allclose(got, dec, rtol=0, atol=1e-2)
+    assert np.abs(got - dec).mean() < 1e-3
+    ref = OA.paged_decode(cs["q"], cs["ko"], cs["vo"], cs["tables"], cs["ctx"], 0.09, "bf16")
+    assert_close(got, ref, "bf16", "one-token prefill")
+    assert_close(dec, ref, "bf16", "decode")
+
+
+def test_prefill_tile_before_the_context_start_next_to_live_tiles():
+    """In one workgroup of query tiles, a tile whose queries all sit before
+    position 0 still writes zeros while its neighbours compute."""
+    cs = _prefill_case((40,), (100,), 4, 4, 128, 16, seed=370)
+    short = cs["ctx"].copy()
+    short[0] = 60  # 100 queries, context 60: queries 0..39 sit before position 0
+    got = _run(cs, 4, 128, 0, 0.1, ctx_dev=torch.from_numpy(short).cuda())
+    ref = OA.paged_prefill(cs["q"], cs["ko"], cs["vo"], cs["tables"], short, cs["starts"], 0.1,
+                           "bf16")
+    assert (got[:40] == 0).all()
+    assert_close(got, ref, "bf16", "tile before position 0")

@@ -73,6 +73,7 @@ class DecodeShape:
     shared_prefix_tokens: int = 0
     num_sharers: int = 0
     partition_size: int = 0             # 0: single pass over each sequence
+    chunk: int = 0                      # > 0: a prefill step of this many new tokens per sequence
     seed: int = 0
 
     @property
@@ -100,6 +101,10 @@ SHAPES: Tuple[DecodeShape, ...] = (
                 ctx_hi=8192, shared_prefix_tokens=1024, num_sharers=128, seed=1003),
     DecodeShape("long_splitk_bf16", "bf16", 32, 64, 8, 128, 16, "uniform", ctx_lo=16384,
                 ctx_hi=32768, partition_size=512, seed=1004),
+    # chunked prefill (not one of the five decode shapes): 16 LLaMA-13B-shaped
+    # sequences each add a 512-token prompt chunk after 0..3584 earlier tokens
+    DecodeShape("prefill_chunk_bf16", "bf16", 16, 40, 40, 128, 16, "uniform", ctx_lo=512,
+                ctx_hi=4096, chunk=512, seed=1005),
 )
 
 
@@ -218,7 +223,9 @@ class Workload:
     ``("add", seq)``, ``("append", seq, n_tokens)``,
     ``("fork", src_seq, dst_seq, n_tokens)``.
     After ``ops``, a step with ``new_tokens`` appends one token per sequence
-    (in sequence order) and writes ``new_k`` / ``new_v`` through the slots.
+    (in sequence order) and writes ``new_k`` / ``new_v`` through the slots; a
+    prefill shape (``chunk`` > 0) appends ``chunk`` tokens per sequence, whose
+    ``q`` rows are ``[B * chunk, Hq, D]`` in sequence order.
     """
 
     shape: DecodeShape
@@ -283,26 +290,28 @@ def make_workload(s: DecodeShape, with_payload: bool = True,
         for b in shared[1:]:
             ops.append(("fork", first, int(b), pre))
     is_sharer = set(int(b) for b in shared)
+    step_tokens_ = s.chunk if s.chunk else (1 if s.new_tokens else 0)
     for b in range(s.num_seqs):
-        n = int(ctx[b]) - (pre if b in is_sharer else 0) - (1 if s.new_tokens else 0)
+        n = int(ctx[b]) - (pre if b in is_sharer else 0) - step_tokens_
         if n > 0:
             ops.append(("append", b, n))
 
     B, Hq, Hkv, D, bs = s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size
     q = k_cache = v_cache = new_k = new_v = None
     if with_payload:
-        q = _payload(s, _S_Q, (B, Hq, D))
+        rows = B * s.chunk if s.chunk else B
+        q = _payload(s, _S_Q, (rows, Hq, D))
         k_cache = _payload(s, _S_K, (n_blocks, bs, Hkv, D))
         v_cache = _payload(s, _S_V, (n_blocks, bs, Hkv, D))
-        if s.new_tokens:
-            new_k = _payload(s, _S_NEWK, (B, Hkv, D))
-            new_v = _payload(s, _S_NEWV, (B, Hkv, D))
+        if s.new_tokens or s.chunk:
+            new_k = _payload(s, _S_NEWK, (rows, Hkv, D))
+            new_v = _payload(s, _S_NEWV, (rows, Hkv, D))
     return Workload(s, ctx, shared, n_blocks, free_order, ops, q, k_cache, v_cache, new_k, new_v)
 
 
 def step_tokens(s: DecodeShape, step: int) -> Tuple[np.ndarray, np.ndarray]:
-    """New K/V rows ``[B, Hkv, D]`` for a later decode step ``step`` >= 1."""
-    shp = (s.num_seqs, s.num_kv_heads, s.head_dim)
+    """New K/V rows ``[B (x chunk), Hkv, D]`` for a later step ``step`` >= 1."""
+    shp = (s.num_seqs * (s.chunk or 1), s.num_kv_heads, s.head_dim)
     return (_payload(dataclasses.replace(s, seed=s.seed * 1000 + step), _S_NEWK, shp),
             _payload(dataclasses.replace(s, seed=s.seed * 1000 + step), _S_NEWV, shp))
 
