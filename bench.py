@@ -121,12 +121,18 @@ def summarize_profile(prefix: str, last: int) -> int:
     return 0
 
 
-def decode_source_hash() -> str:
-    """sha256 of the decode kernels' sources (a traffic record is valid only
-    for the kernels it was measured on)."""
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "attn_common.h", "pkv_device.h"),
+    "prefill": ("prefill.hip", "attn_common.h", "pkv_device.h"),
+}
+
+
+def kernel_source_hash(kind: str) -> str:
+    """sha256 of the sources of the decode or the prefill kernels (a traffic
+    record is valid only for the kernels it was measured on)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode.hip", "pkv_device.h"):
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "paged_kv_cache_292_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -169,7 +175,9 @@ def summarize_counters(fetch_prefix: str, write_prefix: str, last: int, out_json
     # the first block-copy dispatch is the calibration one (the later ones time it)
     f_factor = cal["bytes_read"] / one(fetch, "copy_blocks_kernel")[0][1]
     w_factor = cal["bytes_written"] / one(write, "copy_blocks_kernel")[0][1]
-    parts = ["decode_", "reduce_partitions_kernel"]
+    kind = "prefill" if bench["config"].get("chunk_tokens") else "decode"
+    parts = (["prefill_lds_kernel", "merge_prefill_kernel"] if kind == "prefill"
+             else ["decode_", "reduce_partitions_kernel"])
     fetch_b = sum(np.mean([x[1] for x in v[-last:]]) for k, v in fetch.items()
                   if any(p in k for p in parts))
     write_b = sum(np.mean([x[1] for x in v[-last:]]) for k, v in write.items()
@@ -177,7 +185,7 @@ def summarize_counters(fetch_prefix: str, write_prefix: str, last: int, out_json
     traffic = fetch_b * f_factor + write_b * w_factor
     alg = bench["roofline"]["algorithmic_bytes_per_launch"]
     rec = {"workload": bench["config"]["workload"], "decode_path": bench["config"].get("decode_path"),
-           "kernel_source_sha256": decode_source_hash(),
+           "kernel_source_sha256": kernel_source_hash(kind), "kernels": parts,
            "traffic_bytes_per_launch": int(traffic),
            "fetch_bytes_raw": int(fetch_b), "write_bytes_raw": int(write_b),
            "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
@@ -189,14 +197,14 @@ def summarize_counters(fetch_prefix: str, write_prefix: str, last: int, out_json
     return 0
 
 
-def load_traffic(workload: str, path_name: str):
+def load_traffic(workload: str, path_name: str, kind: str):
     """Stored HBM traffic per launch for this workload, if it was measured on
-    the current decode sources; else None."""
+    the current sources of its kernels; else None."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}_{path_name}.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    if rec.get("kernel_source_sha256") != decode_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(kind):
         return None
     return rec
 
@@ -295,14 +303,18 @@ def main() -> int:
     # per-step algorithmic bytes of the decode call
     E = s.elem_bytes
 
+    qrows = chunk if chunk else 1  # query rows per sequence
+
     def decode_bytes(ctx):
+        """Unique K/V bytes of the step's sequences, and those plus q, out,
+        tables, lengths and (partitioned) the partials written and read back."""
         kv = int(ctx.sum()) * 2 * Hkv * D * E
         nb = int(((ctx + bs - 1) // bs).sum())
-        other = 2 * B * Hq * D * E + 4 * nb + 4 * B
+        other = 2 * B * qrows * Hq * D * E + 4 * nb + 4 * B
         if part_used > 0:
             np_ = (ctx + part_used - 1) // part_used
             multi = np_[np_ > 1].sum()
-            other += int(multi) * Hq * (D + 2) * 4 * 2
+            other += int(multi) * qrows * Hq * (D + 2) * 4 * 2
         return kv, kv + other
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -400,7 +412,7 @@ def main() -> int:
             "head_dim": D, "block_size": bs, "mean_context": round(tok_t / K / B, 1),
             "max_context": max_ctx_final, "new_tokens_per_step": B * step_tok,
             "partition_size": part_used, "kv_bytes_per_step": int(kv_t // K),
-            "decode_path": args.path, "launch_order": args.order,
+            "decode_path": args.path, "launch_order": args.order, "chunk_tokens": chunk,
         },
         "roofline": {
             "kernel": "paged_attention_decode (partition kernel + log-sum-exp merge)",
@@ -424,9 +436,10 @@ def main() -> int:
             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
             "avg_launch_us": round(dec_avg_s * 1e6, 2), "flops_per_launch": int(fl),
             "kv_GBps_unique": round(achieved, 1),
+            "algorithmic_bytes_per_launch": int(alg_per_launch),
         }
         res["prefill_tokens_per_s"] = round(rows * K / elapsed, 1)
-    tr = load_traffic(s.name, args.path)
+    tr = load_traffic(s.name, args.path, "prefill" if chunk else "decode")
     if tr is not None and tr["steps"] == args.steps and tr["warmup"] == args.warmup:
         res["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
     if args.calibrate_copy:

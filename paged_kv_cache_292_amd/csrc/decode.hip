@@ -20,84 +20,18 @@
 // Long contexts are split into partitions handled by separate workgroups;
 // each writes its normalised partial output with its max and sum, and a
 // second kernel merges them by log-sum-exp weights.
-#include <algorithm>
-#include <cfloat>
-
-#include "pkv_device.h"
-#include "pkv_internal.h"
+//
+// Chunked prefill (several queries per sequence) shares the argument block
+// and helpers in attn_common.h and lives in prefill.hip.
+#include "attn_common.h"
 
 namespace pkv {
 namespace {
 
-using namespace dev;
-
-// Workgroup -> (partition, kv head [x query tile], sequence).  The dispatcher
-// deals consecutive workgroups round-robin to the 8 XCDs.  Partitions of one
-// sequence are kept adjacent (they read neighbouring blocks of the same
-// table), and the partition dimension of the grid is odd, so the partitions
-// of consecutive (head, sequence) pairs rotate over the XCDs instead of
-// partition p always landing on XCD p mod 8 (measured: a grid of exactly 8
-// partition columns ran 2.3x slower).  Columns past a sequence's partition
-// count are empty and exit at once.
-inline dim3 work_grid(int parts, int y, int seqs) { return dim3(parts | 1, y, seqs); }
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kChunk = 16;          // tokens per wave iteration
-constexpr int kSingle = 1 << 30;    // "partition" length of single-pass mode
-
-struct DecodeArgs {
-  void* out;
-  const void* q;
-  const void* k_cache;
-  const void* v_cache;
-  const int32_t* tables;
-  const int32_t* ctx_lens;
-  const int32_t* order;  // optional launch order of the sequences (a permutation)
-  const int32_t* query_start;  // prefill: first query row of each sequence [B + 1]
-  int32_t q_tiles;             // prefill: query tiles per sequence (grid y = kv heads x tiles)
-  int32_t total_queries;       // prefill: rows of q / out
-  float* part_o;   // [B, Hq, max_parts, D]
-  float* part_ml;  // [B, Hq, max_parts, 2] (max in log2 units, sum)
-  int32_t num_seqs;
-  int32_t max_blocks;
-  int32_t ctx_cap;  // min(max_context_len, max_blocks * block_size)
-  int32_t num_q_heads;
-  int32_t num_kv_heads;
-  int32_t num_blocks;
-  int32_t partition;  // tokens per partition (multiple of 16), kSingle = one
-  int32_t max_parts;
-  float scale_log2;   // scale * log2(e): logits are kept in base-2 units
-};
-
-// Sequence handled by grid row z: the caller's launch order if given (e.g.
-// longest first, so the longest sequences do not finish last), else z.
-// Entries are clamped into range, so a bad order cannot read out of bounds.
-__device__ __forceinline__ int seq_of(const DecodeArgs& a, int z) {
-  if (!a.order) return z;
-  const int b = scalar_read(a.order + z);
-  return (unsigned)b < (unsigned)a.num_seqs ? b : z;
-}
-
-// Prefill: first query row and query count of sequence b, clamped so that a
-// bad query_start can never address rows outside [0, total_queries).
-__device__ __forceinline__ void query_range(const DecodeArgs& a, int b, int& first, int& count) {
-  int lo = scalar_read(a.query_start + b);
-  int hi = scalar_read(a.query_start + b + 1);
-  lo = lo < 0 ? 0 : (lo > a.total_queries ? a.total_queries : lo);
-  hi = hi < lo ? lo : (hi > a.total_queries ? a.total_queries : hi);
-  first = lo;
-  count = hi - lo;
-}
-
-__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int b) {
-  int c = a.ctx_lens[b];
-  return c < 0 ? 0 : (c > a.ctx_cap ? a.ctx_cap : c);
-}
-
 // ---------------------------------------------------------------------------
 // Partition kernel, query-head group G on the vector ALUs.
 template <typename T, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
   constexpr int EPL = D / 16;                      // elements per lane
   constexpr int WORDS = EPL * int(sizeof(T)) / 4;  // 32-bit words per lane
   using F = Frag<WORDS>;
@@ -343,13 +277,6 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
 // second product; sums and accumulators stay fp32.
 // The q.K^T k order is permuted identically in both operands (lane group c,
 // step j covers dims 8c + 32j .. +7), which leaves the dot product unchanged.
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-typedef float f32x2v_t __attribute__((ext_vector_type(2)));
-
-constexpr float kLazyMax = 8.0f;  // log2 of the largest p allowed before rescaling
 
 // Load flavours of the matrix-core kernel.  Its V loads read whole 256-byte
 // rows per 16 lanes and stream them (non-temporal); its K loads read a 64-byte
@@ -364,13 +291,8 @@ constexpr float kLazyMax = 8.0f;  // log2 of the largest p allowed before rescal
 constexpr bool kMfmaKNT = PKV_MFMA_K_NT;
 constexpr bool kMfmaVNT = PKV_MFMA_V_NT;
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2v_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));  // RNE
-}
-
-template <int D, int BS, int NW, bool PREFILL>
-__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(DecodeArgs a) {
+template <int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 32;  // q.K^T MFMA steps over head_dim
   constexpr int EPL = D / 16;     // V elements per lane per token row = PV tiles
   constexpr int VW = EPL / 2;     // 32-bit words per V load
@@ -380,45 +302,27 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(DecodeArgs a) {
   const int c = lane >> 4;
   const int n = lane & 15;
   const int part = blockIdx.x;
-  const int kvh = PREFILL ? int(blockIdx.y) % a.num_kv_heads : int(blockIdx.y);
-  // decode: the waves of a workgroup split one row tile's tokens; prefill:
-  // each wave owns its own query tile over all tokens (the waves read the
-  // same K/V lines at about the same time and share them through the caches)
-  const int tile = PREFILL ? (int(blockIdx.y) / a.num_kv_heads) * NW + wave : 0;
+  const int kvh = blockIdx.y;
   const int b = seq_of(a, blockIdx.z);
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
 
-  // The 16 operand columns are (query, head) rows: QPT queries of the
-  // sequence's chunk times the G heads of this kv head (decode: one query).
-  // Query qi of a chunk of nq sits at position ctx - nq + qi and attends to
-  // tokens 0 .. that position.
-  const int QPT = PREFILL ? (16 / G > 0 ? 16 / G : 1) : 1;
+  // The 16 operand columns are the G query heads of this kv head (padded
+  // with zero columns); the query sees the sequence's whole context.
   const int ctx = clamp_ctx(a, b);
-  int nq = 1, qrow0 = b;  // queries of this sequence, row of its first query
-  if constexpr (PREFILL) query_range(a, b, qrow0, nq);
-  const int q_first = tile * QPT;
-  if (q_first >= nq) return;  // no query of this sequence in this tile
-  const int q_last = min(q_first + QPT, nq) - 1;
-  const int t_end = max(0, ctx - nq + q_last + 1);  // tokens any row of the tile sees
   const int t0 = part * a.partition;
-  const int t1 = min(t_end, t0 + a.partition);
-  const int nparts = (t_end + a.partition - 1) / a.partition;
-  const int rows = (q_last - q_first + 1) * G;  // valid operand columns
-  // this lane's row n: query q_first + n / G, head n % G; last visible token
+  const int t1 = min(ctx, t0 + a.partition);
+  const int nparts = (ctx + a.partition - 1) / a.partition;
+  const int rows = G;  // valid operand columns
   const bool row_ok = n < rows;
-  const int qi = q_first + (row_ok ? n / G : 0);
-  const int pos_n = row_ok ? ctx - nq + qi : -1;
-  auto out_row = [&](int r) {  // global (query row, head) index of column r
-    return (size_t(qrow0) + q_first + r / G) * Hq + size_t(kvh) * G + r % G;
+  auto out_row = [&](int r) {  // (sequence, query head) index of column r
+    return size_t(b) * Hq + size_t(kvh) * G + r;
   };
   if (t0 >= t1) {
-    if (t_end == 0 && part == 0) {  // nothing visible: zero outputs
-      const int first = PREFILL ? lane : int(threadIdx.x);
-      for (int i = first; i < rows * D; i += PREFILL ? 64 : NW * 64)
+    if (ctx == 0 && part == 0)  // nothing visible: zero outputs
+      for (int i = threadIdx.x; i < rows * D; i += NW * 64)
         store_elem<uint16_t>(a.out, out_row(i / D) * D + i % D, 0.0f);
-    }
     return;
   }
 
@@ -505,7 +409,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tc + 4 * c + i;
-      sc[i] = (t < t1 && (!PREFILL || t <= pos_n)) ? s[i] * a.scale_log2 : -INFINITY;
+      sc[i] = t < t1 ? s[i] * a.scale_log2 : -INFINITY;
     }
     const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if (__ballot(mx > m + kLazyMax)) {  // rare: move the reference max
@@ -541,9 +445,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  constexpr int WSTEP = PREFILL ? 1 : NW;  // chunks between one wave's iterations
+  constexpr int WSTEP = NW;  // chunks between one wave's iterations
   Regs ra, rb;
-  int ch = c_begin + (PREFILL ? 0 : wave);
+  int ch = c_begin + wave;
   if (ch < c_end) {
     load_chunk(ch, ra, true);
     while (true) {
@@ -581,7 +485,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(DecodeArgs a) {
       }
     }
   };
-  if constexpr (NW == 1 || PREFILL) {  // this wave holds all of its rows' tokens
+  if constexpr (NW == 1) {  // this wave holds all of its rows' tokens
     if (row_ok) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -619,285 +523,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Chunked prefill on the matrix cores, K/V shared through LDS.
-//
-// A workgroup of NWP waves owns NWP query tiles (16 (query, head) rows each,
-// as in attn_mfma_kernel) of one (sequence, kv head, partition).  Each
-// 16-token K/V chunk is loaded once by the whole workgroup — whole rows,
-// streamed — into a double-buffered LDS tile, and every wave runs its
-// q.K^T and P.V products on it, so K/V cross the caches once per workgroup
-// instead of once per tile.  The next chunk's loads are in flight while the
-// current one is computed.  Waves whose tile sees no token of a chunk (the
-// causal boundary) skip its math but keep to the barriers.
-template <int D, int BS, int NWP>
-__global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(DecodeArgs a) {
-  constexpr int KSTEPS = D / 32;
-  constexpr int EPL = D / 16;
-  constexpr int VW = EPL / 2;
-  constexpr int RB = D * 2;            // bytes of one token's K (or V) row
-  constexpr int PITCH = RB + 16;       // padded LDS row pitch
-  constexpr int LPR = RB / 16;         // 16-byte pieces per row
-  constexpr int PIECES = 16 * LPR;     // pieces per 16-token chunk, per cache
-  static_assert(2 * PIECES <= NWP * 64 * 2, "chunk loads cover at most two pieces per lane");
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2][16 * PITCH];  // [buffer][K/V]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane >> 4;
-  const int n = lane & 15;
-  const int part = blockIdx.x;
-  const int kvh = int(blockIdx.y) % a.num_kv_heads;
-  const int tile = (int(blockIdx.y) / a.num_kv_heads) * NWP + wave;
-  const int b = seq_of(a, blockIdx.z);
-  const int Hq = a.num_q_heads;
-  const int Hkv = a.num_kv_heads;
-  const int G = Hq / Hkv;
-  const int QPT = 16 / G > 0 ? 16 / G : 1;
-
-  const int ctx = clamp_ctx(a, b);
-  int qrow0, nq;
-  query_range(a, b, qrow0, nq);
-  // workgroup-wide token range: the causal end of its last tile with queries
-  const int g_first = (int(blockIdx.y) / a.num_kv_heads) * NWP * QPT;
-  if (g_first >= nq) return;  // uniform over the workgroup
-  const int g_last = min(g_first + NWP * QPT, nq) - 1;
-  const int t0 = part * a.partition;
-  const int g_end = max(0, ctx - nq + g_last + 1);
-  const int g_t1 = min(g_end, t0 + a.partition);
-
-  // this wave's tile
-  const int q_first = tile * QPT;
-  const bool has_tile = q_first < nq;
-  const int q_last = has_tile ? min(q_first + QPT, nq) - 1 : q_first;
-  const int t_end = has_tile ? max(0, ctx - nq + q_last + 1) : 0;
-  const int t1 = min(t_end, t0 + a.partition);
-  const int nparts = (t_end + a.partition - 1) / a.partition;
-  const int rows = has_tile ? (q_last - q_first + 1) * G : 0;
-  const bool row_ok = n < rows;
-  const int qi = q_first + (row_ok ? n / G : 0);
-  const int pos_n = row_ok ? ctx - nq + qi : -1;
-  auto out_row = [&](int r) {
-    return (size_t(qrow0) + q_first + r / G) * Hq + size_t(kvh) * G + r % G;
-  };
-  if (t0 >= g_t1) {  // uniform: no token of this partition for any tile
-    if (part == 0 && has_tile && t_end == 0)
-      for (int i = lane; i < rows * D; i += 64)
-        store_elem<uint16_t>(a.out, out_row(i / D) * D + i % D, 0.0f);
-    return;
-  }
-
-  uint4 qop[KSTEPS];
-  {
-    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + out_row(row_ok ? n : 0) * D + 8 * c;
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qh + 32 * j);
-      qop[j] = row_ok ? v : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  f32x4_t acc[EPL];
-#pragma unroll
-  for (int t = 0; t < EPL; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -FLT_MAX, l = 0.0f;
-
-  const int row_stride = Hkv * D;
-  const char* kc = static_cast<const char*>(a.k_cache);
-  const char* vc = static_cast<const char*>(a.v_cache);
-  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
-  const int c_begin = t0 / kChunk;
-  const int c_end = (g_t1 + kChunk - 1) / kChunk;
-
-  // Cooperative chunk load: piece p (< 2 * PIECES) of the chunk is 16 bytes of
-  // K (p < PIECES) or V, token p % PIECES / LPR, bytes 16 * (p % LPR).
-  constexpr int PER_LANE = (2 * PIECES + NWP * 64 - 1) / (NWP * 64);
-  uint4 stage[PER_LANE];
-  auto fetch = [&](int ch) {
-    const int tc = __builtin_amdgcn_readfirstlane(ch * kChunk);
-    int bid = scalar_read(tbl + tc / BS);
-    bid = (unsigned)bid < (unsigned)a.num_blocks ? bid : 0;
-    const size_t rowbase = ((size_t(bid) * BS + (tc % BS)) * row_stride + size_t(kvh) * D) * 2;
-#pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) {
-      const int p = threadIdx.x + k * NWP * 64;
-      if (p < 2 * PIECES) {
-        const int pp = p % PIECES;
-        const int tok = pp / LPR;
-        const char* base = (p < PIECES ? kc : vc) + rowbase;
-        // rows past the range re-read the chunk's first row (masked later)
-        const uint32_t off = uint32_t((tc + tok < g_t1 ? tok * row_stride * 2 : 0) + 16 * (pp % LPR));
-        stage[k] = load16<true>(base + off);
-      }
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) {
-      const int p = threadIdx.x + k * NWP * 64;
-      if (p < 2 * PIECES) {
-        const int pp = p % PIECES;
-        *reinterpret_cast<uint4*>(&s_kv[buf][p < PIECES ? 0 : 1][(pp / LPR) * PITCH + 16 * (pp % LPR)]) = stage[k];
-      }
-    }
-  };
-
-  auto compute = [&](int ch, int buf) {
-    const int tc = ch * kChunk;
-    if (tc >= t1) return;  // this tile sees no token of this chunk
-    const char* ks = s_kv[buf][0];
-    const char* vs = s_kv[buf][1];
-    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      const uint4 kop = *reinterpret_cast<const uint4*>(ks + n * PITCH + 16 * c + 64 * j);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
-                                                  __builtin_bit_cast(bf16x8_t, qop[j]), s, 0, 0,
-                                                  0);
-    }
-    uint32_t v[4][VW];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* src = vs + (4 * c + i) * PITCH + EPL * 2 * n;
-      if constexpr (VW == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(src);
-        v[i][0] = x.x;
-        v[i][1] = x.y;
-        v[i][2] = x.z;
-        v[i][3] = x.w;
-      } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(src);
-        v[i][0] = x.x;
-        v[i][1] = x.y;
-      }
-    }
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = tc + 4 * c + i;
-      sc[i] = (t < t1 && t <= pos_n) ? s[i] * a.scale_log2 : -INFINITY;
-    }
-    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    if (__ballot(mx > m + kLazyMax)) {
-      float hm = fmaxf(mx, __shfl_xor(mx, 16));
-      hm = fmaxf(hm, __shfl_xor(hm, 32));
-      const float mn = hm > m + kLazyMax ? hm : m;
-      const float alpha = fast_exp2(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
-      m = mn;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    const s16x4_t pb =
-        __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
-#pragma unroll
-    for (int t = 0; t < EPL; ++t) {
-      const int w = t >> 1;
-      uint32_t lo, hi;
-      if (t & 1) {
-        lo = (v[0][w] >> 16) | (v[1][w] & 0xFFFF0000u);
-        hi = (v[2][w] >> 16) | (v[3][w] & 0xFFFF0000u);
-      } else {
-        lo = (v[0][w] & 0xFFFFu) | (v[1][w] << 16);
-        hi = (v[2][w] & 0xFFFFu) | (v[3][w] << 16);
-      }
-      const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pb, acc[t], 0, 0, 0);
-    }
-  };
-
-  // pipeline: fetch(next) overlaps compute(current); one barrier per chunk
-  fetch(c_begin);
-  store(0);
-  __syncthreads();
-  int buf = 0;
-  for (int ch = c_begin; ch < c_end; ++ch) {
-    const bool more = ch + 1 < c_end;
-    if (more) fetch(ch + 1);
-    compute(ch, buf);
-    if (more) store(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-  }
-
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!has_tile) return;
-  if (t_end == 0) {  // every query of this tile sits before position 0
-    if (part == 0)
-      for (int i = lane; i < rows * D; i += 64)
-        store_elem<uint16_t>(a.out, out_row(i / D) * D + i % D, 0.0f);
-    return;
-  }
-  if (part >= nparts) return;
-  const bool single = nparts == 1;
-  if (row_ok) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int t = 0; t < EPL; ++t) {
-        const int d = EPL * (4 * c + r) + t;
-        const float o = l > 0.0f ? acc[t][r] / l : 0.0f;
-        if (single) {
-          store_elem<uint16_t>(a.out, out_row(n) * D + d, o);
-        } else {
-          const size_t pi = out_row(n) * a.max_parts + part;
-          a.part_o[pi * D + d] = o;
-          if (d == 0) {
-            a.part_ml[2 * pi] = m;
-            a.part_ml[2 * pi + 1] = l;
-          }
-        }
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Log-sum-exp merge of the partitions of one prefill query tile (its valid
-// (query, head) rows), the same weights as the decode merge below.
-template <int D>
-__global__ __launch_bounds__(256) void merge_prefill_kernel(DecodeArgs a) {
-  const int kvh = int(blockIdx.y) % a.num_kv_heads;
-  const int tile = int(blockIdx.y) / a.num_kv_heads;
-  const int b = blockIdx.z;
-  const int Hq = a.num_q_heads;
-  const int G = Hq / a.num_kv_heads;
-  const int QPT = 16 / G > 0 ? 16 / G : 1;
-  const int ctx = clamp_ctx(a, b);
-  int qrow0, nq;
-  query_range(a, b, qrow0, nq);
-  const int q_first = tile * QPT;
-  if (q_first >= nq) return;
-  const int q_last = min(q_first + QPT, nq) - 1;
-  const int t_end = max(0, ctx - nq + q_last + 1);
-  const int nparts = (t_end + a.partition - 1) / a.partition;
-  if (nparts <= 1) return;  // written directly by the partition kernel
-  const int rows = (q_last - q_first + 1) * G;
-  for (int i = threadIdx.x; i < rows * D; i += 256) {
-    const int r = i / D;
-    const int d = i % D;
-    const size_t row = (size_t(qrow0) + q_first + r / G) * Hq + size_t(kvh) * G + r % G;
-    const float* ml = a.part_ml + 2 * row * a.max_parts;
-    const float* po = a.part_o + row * a.max_parts * D;
-    float M = -FLT_MAX;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-    float L = 0.0f, O = 0.0f;
-    for (int p = 0; p < nparts; ++p) {
-      const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-      L += w;
-      O = fmaf(w, po[size_t(p) * D + d], O);
-    }
-    store_elem<uint16_t>(a.out, row * D + d, L > 0.0f ? O / L : 0.0f);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Log-sum-exp merge of the partitions of one (sequence, query head).
 // out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - max_p m_p).
 template <typename T, int D>
-__global__ __launch_bounds__(64) void reduce_partitions_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void reduce_partitions_kernel(AttnArgs a) {
   constexpr int DPT = D / 64;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -931,31 +560,22 @@ __global__ __launch_bounds__(64) void reduce_partitions_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Host side.
-
 #ifndef PKV_DECODE_WAVES
 #define PKV_DECODE_WAVES 4
 #endif
-#ifndef PKV_AUTO_PARTITION
-#define PKV_AUTO_PARTITION 2048
-#endif
 constexpr int kNW = PKV_DECODE_WAVES;  // waves per workgroup
 
-// Query tiles (one wave each) per prefill workgroup: as many as the longest
-// chunk fills, up to 16, so every K/V chunk read from HBM serves up to 16
-// tiles.
-int prefill_waves(int q_tiles) { return q_tiles > 8 ? 16 : q_tiles > 4 ? 8 : 4; }
-
 template <typename T, int D, int BS, int G>
-hipError_t launch_valu(const DecodeArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
+hipError_t launch_valu(const AttnArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
   const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
   hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kNW>), grid, dim3(kNW * 64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D, int BS>
-hipError_t launch_mfma(const DecodeArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
+hipError_t launch_mfma(const AttnArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
   const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((attn_mfma_kernel<D, BS, kNW, false>), grid, dim3(kNW * 64), 0, st, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW>), grid, dim3(kNW * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -974,7 +594,7 @@ bool use_mfma(bool bf16, int G) {
 }
 
 template <typename T, int D, int BS>
-hipError_t dispatch_group(const DecodeArgs& a, int G, int num_seqs, hipStream_t st,
+hipError_t dispatch_group(const AttnArgs& a, int G, int num_seqs, hipStream_t st,
                           int grid_parts) {
   if constexpr (sizeof(T) == 2) {
     if (use_mfma(true, G)) return launch_mfma<D, BS>(a, num_seqs, st, grid_parts);
@@ -989,32 +609,14 @@ hipError_t dispatch_group(const DecodeArgs& a, int G, int num_seqs, hipStream_t 
 }
 
 template <typename T, int D>
-hipError_t dispatch_bs(const DecodeArgs& a, int BS, int G, int num_seqs, hipStream_t st,
+hipError_t dispatch_bs(const AttnArgs& a, int BS, int G, int num_seqs, hipStream_t st,
                        int grid_parts) {
   return BS == 16 ? dispatch_group<T, D, 16>(a, G, num_seqs, st, grid_parts)
                   : dispatch_group<T, D, 32>(a, G, num_seqs, st, grid_parts);
 }
 
-template <int D, int BS>
-hipError_t launch_prefill(const DecodeArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
-  const int nw = prefill_waves(a.q_tiles);
-  const int groups = (a.q_tiles + nw - 1) / nw;
-  const dim3 grid = work_grid(grid_parts, a.num_kv_heads * groups, num_seqs);
-  if (nw == 16)
-    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, 16>), grid, dim3(16 * 64), 0, st, a);
-  else if (nw == 8)
-    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, 8>), grid, dim3(8 * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, 4>), grid, dim3(4 * 64), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.partition >= kSingle) return e;
-  hipLaunchKernelGGL((merge_prefill_kernel<D>), dim3(1, a.num_kv_heads * a.q_tiles, num_seqs),
-                     dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
 template <typename T, int D>
-hipError_t launch_reduce(const DecodeArgs& a, int num_seqs, hipStream_t st) {
+hipError_t launch_reduce(const AttnArgs& a, int num_seqs, hipStream_t st) {
   hipLaunchKernelGGL((reduce_partitions_kernel<T, D>), dim3(a.num_q_heads, num_seqs), dim3(64),
                      0, st, a);
   return hipGetLastError();
@@ -1025,162 +627,10 @@ bool group_supported(bool bf16, int g) {
   return bf16 && g >= 2 && g <= 16;
 }
 
-// Partition length actually used, 0 = single pass.  AUTO splits contexts
-// longer than 2048 tokens into 2048-token partitions (measured on MI355X over
-// the five decode shapes with a longest-first launch order).
-int32_t resolve_partition(int32_t max_context_len, int32_t partition_size) {
-  if (partition_size == PKV_PARTITION_AUTO)
-    return max_context_len > PKV_AUTO_PARTITION ? PKV_AUTO_PARTITION : 0;
-  return partition_size;
-}
-
-size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                     int32_t max_context_len, int32_t partition) {
-  if (partition <= 0 || max_context_len <= 0) return 0;
-  const size_t parts = size_t((int64_t(max_context_len) + partition - 1) / partition);
-  const size_t heads = size_t(num_seqs) * size_t(num_q_heads);
-  return heads * parts * (size_t(head_dim) + 2) * sizeof(float);
-}
-
 }  // namespace
 }  // namespace pkv
 
 using pkv::fail;
-
-namespace pkv {
-namespace {
-// Partition size of a prefill call.  AUTO: the query tiles already give the
-// grid enough workgroups in most cases and splitting the tokens only adds
-// merge work, so partitions are used only when there are fewer than about
-// four workgroups per CU.
-int32_t prefill_partition(int32_t num_seqs, int32_t max_queries_per_seq, int32_t num_q_heads,
-                          int32_t num_kv_heads, int32_t max_context_len,
-                          int32_t partition_size) {
-  if (partition_size != PKV_PARTITION_AUTO || num_kv_heads <= 0 || num_q_heads <= 0)
-    return resolve_partition(max_context_len, partition_size);
-  const int G = num_q_heads / num_kv_heads;
-  const int qpt = 16 / G > 0 ? 16 / G : 1;
-  const int64_t tiles = (int64_t(max_queries_per_seq) + qpt - 1) / qpt;
-  const int64_t nw = prefill_waves(int(std::min<int64_t>(tiles, 1 << 20)));
-  const int64_t groups = (tiles + nw - 1) / nw;
-  return int64_t(num_seqs) * num_kv_heads * groups >= 1024
-             ? 0
-             : resolve_partition(max_context_len, partition_size);
-}
-}  // namespace
-}  // namespace pkv
-
-extern "C" int32_t pkv_prefill_partition_size(int32_t num_seqs, int32_t max_queries_per_seq,
-                                              int32_t num_q_heads, int32_t num_kv_heads,
-                                              int32_t max_context_len, int32_t partition_size) {
-  return pkv::prefill_partition(num_seqs, max_queries_per_seq, num_q_heads, num_kv_heads,
-                                max_context_len, partition_size);
-}
-
-extern "C" size_t pkv_prefill_workspace_bytes(int32_t total_queries, int32_t num_q_heads,
-                                              int32_t head_dim, int32_t max_context_len,
-                                              int32_t partition_size) {
-  if (total_queries <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return pkv::workspace_for(total_queries, num_q_heads, head_dim, max_context_len,
-                            pkv::resolve_partition(max_context_len, partition_size));
-}
-
-extern "C" pkv_status pkv_paged_attention_prefill(
-    void* out, const void* q, const int32_t* query_start, int32_t total_queries,
-    int32_t max_queries_per_seq, const void* k_cache, const void* v_cache,
-    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-    void* stream) {
-  if (dtype != PKV_BF16)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_prefill: bf16 only (matrix cores)");
-  if (num_seqs < 0 || num_seqs > 65535 || total_queries < 0 || max_queries_per_seq < 0)
-    return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_prefill: num_seqs=%d total_queries=%d max_queries_per_seq=%d",
-                num_seqs, total_queries, max_queries_per_seq);
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-      num_q_heads / num_kv_heads > 16)
-    return fail(PKV_ERR_UNSUPPORTED,
-                "paged_attention_prefill: num_q_heads=%d / num_kv_heads=%d must be a group of 1..16",
-                num_q_heads, num_kv_heads);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_prefill: head_dim=%d (64 or 128)", head_dim);
-  if (block_size != 16 && block_size != 32)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_prefill: block_size=%d (16 or 32)",
-                block_size);
-  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-      max_context_len > (1 << 29))
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_prefill: bad pool or context sizes");
-  if (partition_size < PKV_PARTITION_AUTO ||
-      (partition_size > 0 && partition_size % block_size != 0))
-    return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_prefill: partition_size=%d must be 0, -1 or a multiple of %d",
-                partition_size, block_size);
-  if (num_seqs == 0 || total_queries == 0 || max_queries_per_seq == 0) return pkv::ok();
-  if (!out || !q || !query_start || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_prefill: NULL pointer argument");
-  const int G = num_q_heads / num_kv_heads;
-  const int qpt = 16 / G > 0 ? 16 / G : 1;
-  const int64_t tiles = (int64_t(max_queries_per_seq) + qpt - 1) / qpt;
-  if (tiles * num_kv_heads > 65535)
-    return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_prefill: %lld query tiles x %d kv heads exceed the grid limit",
-                (long long)tiles, num_kv_heads);
-  const int32_t partition = pkv::prefill_partition(num_seqs, max_queries_per_seq, num_q_heads,
-                                                   num_kv_heads, max_context_len, partition_size);
-  const int32_t cap = int32_t(std::min<int64_t>(max_context_len,
-                                                int64_t(max_blocks_per_seq) * block_size));
-  pkv::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.tables = block_tables;
-  a.ctx_lens = context_lens;
-  a.order = seq_order;
-  a.query_start = query_start;
-  a.q_tiles = int32_t(tiles);
-  a.total_queries = total_queries;
-  a.num_seqs = num_seqs;
-  a.max_blocks = max_blocks_per_seq;
-  a.ctx_cap = cap;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.num_blocks = num_blocks;
-  a.scale_log2 = scale * pkv::kLog2e;
-  int grid_parts = 1;
-  if (partition > 0) {
-    const size_t need =
-        pkv::workspace_for(total_queries, num_q_heads, head_dim, max_context_len, partition);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-      return fail(PKV_ERR_WORKSPACE,
-                  "paged_attention_prefill: workspace of %zu bytes needed, %zu given", need,
-                  workspace ? workspace_bytes : size_t(0));
-    a.partition = partition;
-    a.max_parts = int32_t((int64_t(max_context_len) + partition - 1) / partition);
-    if (a.max_parts < 1) a.max_parts = 1;
-    float* ws = static_cast<float*>(workspace);
-    a.part_o = ws;
-    a.part_ml = ws + size_t(total_queries) * num_q_heads * a.max_parts * head_dim;
-    grid_parts = int((int64_t(cap) + partition - 1) / partition);
-    if (grid_parts < 1) grid_parts = 1;
-  } else {
-    a.partition = pkv::kSingle;
-    a.max_parts = 1;
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (head_dim == 64)
-    e = block_size == 16 ? pkv::launch_prefill<64, 16>(a, num_seqs, st, grid_parts)
-                         : pkv::launch_prefill<64, 32>(a, num_seqs, st, grid_parts);
-  else
-    e = block_size == 16 ? pkv::launch_prefill<128, 16>(a, num_seqs, st, grid_parts)
-                         : pkv::launch_prefill<128, 32>(a, num_seqs, st, grid_parts);
-  if (e != hipSuccess)
-    return fail(PKV_ERR_HIP, "paged_attention_prefill: launch failed: %s", hipGetErrorString(e));
-  return pkv::ok();
-}
 
 extern "C" pkv_status pkv_set_decode_path(int32_t path) {
   if (path != PKV_PATH_AUTO && path != PKV_PATH_VALU && path != PKV_PATH_MFMA)
@@ -1255,7 +705,7 @@ extern "C" pkv_status pkv_paged_attention_decode(
   const int32_t partition = pkv::resolve_partition(max_context_len, partition_size);
   const int32_t cap = int32_t(std::min<int64_t>(max_context_len,
                                                 int64_t(max_blocks_per_seq) * block_size));
-  pkv::DecodeArgs a{};
+  pkv::AttnArgs a{};
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
