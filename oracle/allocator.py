@@ -31,6 +31,24 @@ Readings where the pages are silent (also listed in the design notes):
   copy-on-write);
 * a failing call changes nothing.
 
+Preemption by swapping ("What Is vLLM …", section "What is continuous
+batching in vLLM?", step 2: under memory pressure low-priority sequences are
+preempted and their KV caches moved to CPU memory).  The pages give no
+mechanism; the reading here:
+
+* a second pool of blocks in host memory, with its own first-in first-out
+  free list (``host_free_order``, ascending ids when not given);
+* ``swap_out(seqs)`` visits the sequences' device blocks sequence by
+  sequence, in table order; each distinct block gets one host block (blocks
+  shared inside the group stay shared), and the (device, host) pair is
+  reported for the copy; each holder's reference moves to the host block, and
+  a device block whose count drops to zero goes to the tail of the device
+  free list (a block also held outside the group is copied but stays);
+* ``swap_in(seqs)`` does the same in the other direction with fresh device
+  blocks, reporting (host, device) pairs;
+* a swapped-out sequence cannot grow, fork or be listed in block tables
+  until it is swapped in; freeing it releases its host blocks.
+
 Token ``pos`` of a sequence is stored at slot ``table[pos // bs] * bs + pos % bs``.
 Test infrastructure only.
 """
@@ -41,7 +59,7 @@ from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["AllocatorError", "OutOfBlocks", "NotFound", "SharedWrite", "InvalidArg",
+__all__ = ["AllocatorError", "OutOfBlocks", "NotFound", "SharedWrite", "InvalidArg", "Swapped",
            "BlockAllocator", "slot_of", "blocks_for"]
 
 
@@ -63,6 +81,10 @@ class SharedWrite(AllocatorError):
 
 class InvalidArg(AllocatorError):
     pass
+
+
+class Swapped(AllocatorError):
+    """The sequence is swapped out (or, for a swap-in, is not)."""
 
 
 def blocks_for(num_tokens: int, block_size: int) -> int:
@@ -90,6 +112,31 @@ class BlockAllocator:
         self.refcount: List[int] = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lengths: Dict[int, int] = {}
+        # host pool for swapped-out sequences (absent until set)
+        self.num_host_blocks: Optional[int] = None
+        self.host_free: deque = deque()
+        self.host_refcount: List[int] = []
+        self.swapped: set = set()
+
+    def set_host_pool(self, num_host_blocks: int,
+                      host_free_order: Optional[Iterable[int]] = None) -> None:
+        if self.num_host_blocks is not None:
+            raise InvalidArg("the host pool is already set")
+        if num_host_blocks < 0:
+            raise InvalidArg("negative host pool size")
+        order = (list(range(num_host_blocks)) if host_free_order is None
+                 else [int(b) for b in host_free_order])
+        if sorted(order) != list(range(num_host_blocks)):
+            raise InvalidArg("host_free_order must be a permutation of the host pool ids")
+        self.num_host_blocks = num_host_blocks
+        self.host_free = deque(order)
+        self.host_refcount = [0] * num_host_blocks
+
+    def _resident(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise NotFound(seq)
+        if seq in self.swapped:
+            raise Swapped(f"sequence {seq} is swapped out")
 
     # -- queries -----------------------------------------------------------
     def num_free_blocks(self) -> int:
@@ -119,8 +166,7 @@ class BlockAllocator:
 
     def append(self, seq: int, n: int) -> List[int]:
         """Grow ``seq`` by ``n`` tokens; returns their slots in order."""
-        if seq not in self.tables:
-            raise NotFound(seq)
+        self._resident(seq)
         if n < 0:
             raise InvalidArg("negative token count")
         table = self.tables[seq]
@@ -144,8 +190,7 @@ class BlockAllocator:
     def append_cow(self, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
         """Grow ``seq`` by ``n`` tokens, copying a shared, partly filled last
         block first.  Returns (slots, copy pairs (source block, new block))."""
-        if seq not in self.tables:
-            raise NotFound(seq)
+        self._resident(seq)
         if n < 0:
             raise InvalidArg("negative token count")
         table = self.tables[seq]
@@ -169,6 +214,8 @@ class BlockAllocator:
         """Make ``dst`` (empty) share the first ``num_tokens`` tokens of ``src``."""
         if src not in self.tables or dst not in self.tables:
             raise NotFound((src, dst))
+        self._resident(src)
+        self._resident(dst)
         bs = self.block_size
         whole = num_tokens % bs == 0 or num_tokens == self.lengths[src]
         if (num_tokens < 0 or not whole or num_tokens > self.lengths[src]
@@ -183,16 +230,84 @@ class BlockAllocator:
     def free_seq(self, seq: int) -> None:
         if seq not in self.tables:
             raise NotFound(seq)
-        for blk in self.tables.pop(seq):
-            self.refcount[blk] -= 1
-            if self.refcount[blk] == 0:
-                self.free.append(blk)
+        if seq in self.swapped:
+            self.swapped.discard(seq)
+            for blk in self.tables.pop(seq):
+                self.host_refcount[blk] -= 1
+                if self.host_refcount[blk] == 0:
+                    self.host_free.append(blk)
+        else:
+            for blk in self.tables.pop(seq):
+                self.refcount[blk] -= 1
+                if self.refcount[blk] == 0:
+                    self.free.append(blk)
         del self.lengths[seq]
+
+    def _check_group(self, seqs: Sequence[int], want_swapped: bool) -> None:
+        if self.num_host_blocks is None:
+            raise InvalidArg("no host pool")
+        if len(set(seqs)) != len(seqs):
+            raise InvalidArg("a sequence is listed twice")
+        for s in seqs:
+            if s not in self.tables:
+                raise NotFound(s)
+            if (s in self.swapped) != want_swapped:
+                raise Swapped(f"sequence {s} is in the wrong state for this swap")
+
+    def swap_out(self, seqs: Sequence[int]) -> List[Tuple[int, int]]:
+        """Move the sequences' blocks to the host pool; returns the
+        (device block, host block) copies to make."""
+        self._check_group(seqs, want_swapped=False)
+        distinct = {blk for s in seqs for blk in self.tables[s]}
+        if len(distinct) > len(self.host_free):
+            raise OutOfBlocks(f"need {len(distinct)} host blocks, {len(self.host_free)} free")
+        to_host: Dict[int, int] = {}
+        pairs = []
+        for s in seqs:
+            new_table = []
+            for blk in self.tables[s]:
+                if blk not in to_host:
+                    to_host[blk] = self.host_free.popleft()
+                    pairs.append((blk, to_host[blk]))
+                self.host_refcount[to_host[blk]] += 1
+                self.refcount[blk] -= 1
+                if self.refcount[blk] == 0:
+                    self.free.append(blk)
+                new_table.append(to_host[blk])
+            self.tables[s] = new_table
+            self.swapped.add(s)
+        return pairs
+
+    def swap_in(self, seqs: Sequence[int]) -> List[Tuple[int, int]]:
+        """Move swapped-out sequences back to fresh device blocks; returns the
+        (host block, device block) copies to make."""
+        self._check_group(seqs, want_swapped=True)
+        distinct = {blk for s in seqs for blk in self.tables[s]}
+        if len(distinct) > len(self.free):
+            raise OutOfBlocks(f"need {len(distinct)} device blocks, {len(self.free)} free")
+        to_dev: Dict[int, int] = {}
+        pairs = []
+        for s in seqs:
+            new_table = []
+            for blk in self.tables[s]:
+                if blk not in to_dev:
+                    to_dev[blk] = self.free.popleft()
+                    pairs.append((blk, to_dev[blk]))
+                self.refcount[to_dev[blk]] += 1
+                self.host_refcount[blk] -= 1
+                if self.host_refcount[blk] == 0:
+                    self.host_free.append(blk)
+                new_table.append(to_dev[blk])
+            self.tables[s] = new_table
+            self.swapped.discard(s)
+        return pairs
 
     def build_block_tables(self, seqs: Sequence[int], max_blocks: int,
                            pad: int = -1) -> Tuple[np.ndarray, np.ndarray]:
         tables = np.full((len(seqs), max_blocks), pad, dtype=np.int32)
         ctx = np.zeros(len(seqs), dtype=np.int32)
+        for s in seqs:
+            self._resident(s)
         for i, s in enumerate(seqs):
             t = self.table(s)
             if len(t) > max_blocks:
@@ -212,5 +327,9 @@ class BlockAllocator:
                 self.fork_prefix(op[1], op[2], op[3])
             elif op[0] == "append_cow":
                 self.append_cow(op[1], op[2])
+            elif op[0] == "swap_out":
+                self.swap_out(list(op[1]))
+            elif op[0] == "swap_in":
+                self.swap_in(list(op[1]))
             else:
                 raise InvalidArg(op)

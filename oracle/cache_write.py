@@ -5,13 +5,19 @@ slot the allocator handed out for its position, i.e. row ``slot % block_size``
 of physical block ``slot // block_size`` ("vLLM in Production …", section
 "PagedAttention — Virtual Memory for the KV Cache": blocks are filled as
 tokens arrive).  A negative slot marks a padding token that is not written.
-Every other byte of the cache is left as it was.  Test infrastructure only.
+Every other byte of the cache is left as it was.
+
+Swapping a preempted sequence moves its blocks whole between the device cache
+and a cache pool in host memory ("What Is vLLM …", section "What is
+continuous batching in vLLM?", step 2): ``move_blocks`` is that copy, block
+``dst`` of the target pool becoming block ``src`` of the source pool for each
+(src, dst) pair.  Test infrastructure only.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["reshape_and_cache"]
+__all__ = ["reshape_and_cache", "move_blocks"]
 
 
 def reshape_and_cache(key: np.ndarray, value: np.ndarray, k_cache: np.ndarray,
@@ -30,3 +36,16 @@ def reshape_and_cache(key: np.ndarray, value: np.ndarray, k_cache: np.ndarray,
         kc[slot // bs, slot % bs] = key[i]
         vc[slot // bs, slot % bs] = value[i]
     return kc, vc
+
+
+def move_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                pairs) -> tuple:
+    """Return copies of the target pools ``dst_k, dst_v [M, bs, Hkv, D]`` in
+    which block ``d`` holds block ``s`` of ``src_k, src_v [N, bs, Hkv, D]``
+    for each pair ``(s, d)``; every other block is left as it was."""
+    k = dst_k.copy()
+    v = dst_v.copy()
+    for s, d in pairs:
+        k[int(d)] = src_k[int(s)]
+        v[int(d)] = src_v[int(s)]
+    return k, v

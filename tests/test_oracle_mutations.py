@@ -11,6 +11,7 @@ import pytest
 import test_oracle_allocator as TAL
 import test_oracle_attention as TA
 import test_oracle_cache_write as TC
+import test_oracle_swap as TS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -103,3 +104,42 @@ def test_allocator_mutant_caught(old, new, monkeypatch):
     m = _mutant("oracle/allocator.py", old, new)
     monkeypatch.setattr(TAL, "OAL", m)
     assert _caught([getattr(TAL, n) for n in ALLOC_PINS])
+
+
+SWAP_ALLOC = [
+    ("                if blk not in to_host:\n", "                if True:\n"),
+    ("to_host[blk] = self.host_free.popleft()", "to_host[blk] = self.host_free.pop()"),
+    ("to_dev[blk] = self.free.popleft()", "to_dev[blk] = self.free.pop()"),
+    ("                self.refcount[blk] -= 1\n                if self.refcount[blk] == 0:\n"
+     "                    self.free.append(blk)\n                new_table.append(to_host[blk])",
+     "                self.refcount[blk] -= 1\n                new_table.append(to_host[blk])"),
+    ("                self.host_refcount[blk] -= 1\n                if self.host_refcount[blk] == 0:\n"
+     "                    self.host_free.append(blk)\n                new_table.append(to_dev[blk])",
+     "                new_table.append(to_dev[blk])"),
+    ("            self.swapped.add(s)\n", "\n"),
+    ("            self.swapped.discard(s)\n        return pairs", "\n        return pairs"),
+    ("        self._resident(seq)\n        if n < 0:", "        if n < 0:"),
+    ("if len(distinct) > len(self.host_free):", "if len(distinct) > len(self.host_free) + 1:"),
+    ("        if seq in self.swapped:\n            self.swapped.discard(seq)",
+     "        if False:\n            self.swapped.discard(seq)"),
+    ("pairs.append((blk, to_host[blk]))", "pairs.append((to_host[blk], blk))"),
+]
+
+
+@pytest.mark.parametrize("old,new", SWAP_ALLOC, ids=[f"swapa{i}" for i in range(len(SWAP_ALLOC))])
+def test_swap_allocator_mutant_caught(old, new, monkeypatch):
+    monkeypatch.setattr(TS, "OAL", _mutant("oracle/allocator.py", old, new))
+    assert _caught(TS.PINS)
+
+
+SWAP_MOVE = [
+    ("k[int(d)] = src_k[int(s)]", "k[int(s)] = src_k[int(d)]"),
+    ("v[int(d)] = src_v[int(s)]", "v[int(d)] = src_k[int(s)]"),
+    ("    k = dst_k.copy()\n", "    k = src_k.copy()\n"),
+]
+
+
+@pytest.mark.parametrize("old,new", SWAP_MOVE, ids=[f"swapm{i}" for i in range(len(SWAP_MOVE))])
+def test_swap_move_mutant_caught(old, new, monkeypatch):
+    monkeypatch.setattr(TS, "OC", _mutant("oracle/cache_write.py", old, new))
+    assert _caught(TS.PINS)
