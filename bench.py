@@ -47,6 +47,9 @@ def _args():
     ap.add_argument("--staging-depth", type=int, default=8,
                     help="pinned staging buffers in flight (steps the host may run ahead)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure preemption swapping instead: a quarter of the sequences "
+                         "swapped out to pinned host memory and back, per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy a known number of cache blocks with the "
@@ -209,6 +212,113 @@ def load_traffic(workload: str, path_name: str, kind: str):
     return rec
 
 
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, per direction, published
+
+
+def run_swap(args) -> int:
+    """Swap round trips of the shape's batch: every step, the host allocator
+    swaps a quarter of the sequences out (every 4th, shared blocks once),
+    the swap kernel copies their blocks to the pinned host pool, then they
+    are swapped back in to fresh device blocks.  Kernel times by HIP events
+    on the launch stream; a contiguous runtime copy (DMA engine) of the same
+    bytes in each direction is timed beside it for reference."""
+    import torch
+    import paged_kv_cache_292_amd as P
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = W.shape(args.shape)
+    # headroom: blocks a swapped sequence shares with a resident one stay on
+    # the device, and swap-in gives the swapped sequence fresh copies
+    wl = W.make_workload(s, with_payload=False, extra_tokens=1024)
+    B, Hkv, D, bs = s.num_seqs, s.num_kv_heads, s.head_dim, s.block_size
+    tdt = torch.float32 if s.dtype == "f32" else torch.bfloat16
+    N = wl.num_blocks
+    k_cache = torch.randn((N, bs, Hkv, D), device=dev).to(tdt)
+    v_cache = torch.randn((N, bs, Hkv, D), device=dev).to(tdt)
+    alloc = P.Allocator(N, bs, wl.free_order)
+    alloc.replay(wl.ops)
+    group = list(range(0, B, 4))
+    nh = sum(alloc.num_blocks_of(g) for g in group)
+    alloc.set_host_pool(nh)
+    k_host = torch.empty((nh, bs, Hkv, D), dtype=tdt).pin_memory()
+    v_host = torch.empty((nh, bs, Hkv, D), dtype=tdt).pin_memory()
+    stream = torch.cuda.current_stream()
+    block_bytes = bs * Hkv * D * s.elem_bytes
+    t_out, t_in, h_out, h_in, moved = [], [], [], [], []
+    for i in range(args.warmup + args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        t0 = time.perf_counter()
+        po = alloc.swap_out(group)
+        t1 = time.perf_counter()
+        d_po = torch.from_numpy(po).to(dev)
+        e[0].record(stream)
+        P.swap_blocks(k_cache, v_cache, k_host, v_host, d_po, P.SWAP_OUT)
+        e[1].record(stream)
+        t2 = time.perf_counter()
+        pi = alloc.swap_in(group)
+        t3 = time.perf_counter()
+        d_pi = torch.from_numpy(pi).to(dev)
+        e[2].record(stream)
+        P.swap_blocks(k_cache, v_cache, k_host, v_host, d_pi, P.SWAP_IN)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            t_out.append(e[0].elapsed_time(e[1]) * 1e-3)
+            t_in.append(e[2].elapsed_time(e[3]) * 1e-3)
+            h_out.append(t1 - t0)
+            h_in.append(t3 - t2)
+            moved.append(len(po))
+    nbytes = 2 * int(np.mean(moved)) * block_bytes  # K and V, one direction
+    # DMA reference: one contiguous runtime copy of the same bytes each way
+    flat_h = k_host.view(-1).view(torch.uint8)[: nbytes // 2]
+    flat_h2 = v_host.view(-1).view(torch.uint8)[: nbytes // 2]
+    flat_d = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
+    flat_d2 = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
+    dma = {"h2d": [], "d2h": []}
+    for i in range(args.warmup + args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        flat_d.copy_(flat_h, non_blocking=True)
+        flat_d2.copy_(flat_h2, non_blocking=True)
+        e[1].record(stream)
+        e[2].record(stream)
+        flat_h.copy_(flat_d, non_blocking=True)
+        flat_h2.copy_(flat_d2, non_blocking=True)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            dma["h2d"].append(e[0].elapsed_time(e[1]) * 1e-3)
+            dma["d2h"].append(e[2].elapsed_time(e[3]) * 1e-3)
+    out_gbs = nbytes / float(np.mean(t_out)) / 1e9
+    in_gbs = nbytes / float(np.mean(t_in)) / 1e9
+    res = {
+        "metric": "KV swap bandwidth: device <-> pinned host blocks, swap kernel",
+        "value": round(2 * nbytes / (float(np.mean(t_out)) + float(np.mean(t_in))) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((float(np.mean(t_out)) + float(np.mean(t_in))) * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
+        "data": "synthetic (random cache contents; the shape's length mix and placement)",
+        "config": {"workload": s.name, "num_seqs": B, "swapped_seqs": len(group),
+                   "blocks_per_direction": int(np.mean(moved)), "block_bytes": block_bytes,
+                   "bytes_per_direction": nbytes},
+        "swap_out_GBps": round(out_gbs, 2), "swap_in_GBps": round(in_gbs, 2),
+        "swap_out_us": round(float(np.mean(t_out)) * 1e6, 1),
+        "swap_in_us": round(float(np.mean(t_in)) * 1e6, 1),
+        "host_allocator_us": {"swap_out": round(float(np.mean(h_out)) * 1e6, 1),
+                              "swap_in": round(float(np.mean(h_in)) * 1e6, 1)},
+        "dma_reference_GBps": {"h2d": round(nbytes / float(np.mean(dma["h2d"])) / 1e9, 2),
+                               "d2h": round(nbytes / float(np.mean(dma["d2h"])) / 1e9, 2)},
+        "roofline": {"bound": "host link", "achieved": round(min(out_gbs, in_gbs), 2),
+                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(min(out_gbs, in_gbs) / HOST_LINK_PEAK_GBS, 4), "traffic": None},
+    }
+    alloc.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     args = _args()
     if args.summarize_profile:
@@ -219,6 +329,8 @@ def main() -> int:
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         return 2
+    if args.swap:
+        return run_swap(args)
     import torch
     import paged_kv_cache_292_amd as P
     import workloads as W

@@ -48,7 +48,8 @@ typedef enum pkv_status {
   PKV_ERR_NOT_FOUND = -4,    /* unknown sequence id                            */
   PKV_ERR_SHARED_WRITE = -5, /* append into a block another sequence holds     */
   PKV_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required     */
-  PKV_ERR_HIP = -7           /* a HIP runtime call or kernel launch failed     */
+  PKV_ERR_HIP = -7,          /* a HIP runtime call or kernel launch failed     */
+  PKV_ERR_SWAPPED = -8       /* the sequence is (or is not) swapped out         */
 } pkv_status;
 
 typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -257,6 +258,35 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
 pkv_status pkv_upload_pinned(void* dst, const void* src_host, size_t bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Swap copy: moves whole blocks between the device cache and a cache pool in
+ * pinned host memory, the data movement of preemption by swapping ("What Is
+ * vLLM …", section "What is continuous batching in vLLM?", step 2: under
+ * memory pressure low-priority sequences are preempted and their KV caches
+ * moved to CPU memory; its configuration list sizes that CPU space).
+ *
+ * direction PKV_SWAP_OUT: host[dst] = device[src] for each (src, dst) pair;
+ * PKV_SWAP_IN: device[dst] = host[src].  The pairs come from
+ * pkv_swap_out / pkv_swap_in below.
+ * k_cache, v_cache  device, [num_blocks, block_size, num_kv_heads, head_dim].
+ * k_host, v_host    pinned, mapped host memory (hipHostMalloc, or a torch
+ *                   tensor from pin_memory()), [num_host_blocks, block_size,
+ *                   num_kv_heads, head_dim]; the caller owns both pools.
+ * pairs             device, int64 [num_pairs, 2]; a pair with an id outside
+ *                   its pool is skipped; destinations must be distinct.
+ * Runs as a kernel on `stream` that reads or writes the host pool over the
+ * host link; nothing else synchronizes.  The caller must not touch the host
+ * blocks involved until the copy has run.  PKV_ERR_INVALID_ARG (nothing
+ * launched) if a host pool is not pinned, mapped memory.
+ * ---------------------------------------------------------------------- */
+#define PKV_SWAP_OUT 0
+#define PKV_SWAP_IN 1
+pkv_status pkv_swap_blocks(void* k_cache, void* v_cache, void* k_host, void* v_host,
+                           const int64_t* pairs, int32_t num_pairs, int32_t num_blocks,
+                           int32_t num_host_blocks, int32_t block_size,
+                           int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                           int32_t direction, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block allocator (host memory only; single-threaded use).
  *
  * Fixed-size blocks are handed out one at a time as a sequence grows; a
@@ -348,12 +378,52 @@ pkv_status pkv_decode_step_prepare(pkv_allocator* a, const int64_t* seq_ids,
                                    int32_t* tables_out, int32_t* context_lens_out,
                                    int32_t* max_context_len_out, int32_t* order_out);
 
+/* ------------------------------------------------------------------------
+ * Preemption by swapping ("What Is vLLM …", section "What is continuous
+ * batching in vLLM?", step 2).  The allocator also manages a pool of
+ * num_host_blocks blocks in host memory with its own first-in first-out
+ * free list (host_free_order, a permutation, or ascending when NULL).
+ *
+ * pkv_swap_out moves the listed sequences (distinct, resident) to host
+ * blocks: their device blocks are visited sequence by sequence in table
+ * order; each distinct device block gets one host block (blocks shared
+ * inside the group stay shared, one copy), reported as a (device, host) pair
+ * in pairs_out (host int64 [max_pairs, 2]) and *num_pairs_out; the
+ * sequences' tables then hold the host blocks, and each device block loses
+ * one reference per holder in the group (freed at zero, in visiting order).
+ * A device block also held by a sequence outside the group is still copied
+ * and stays with that sequence.  pkv_swap_in does the reverse with fresh
+ * device blocks: (host, device) pairs, host blocks freed at zero.
+ * The caller runs pkv_swap_blocks over the pairs before anything can write
+ * into the freed blocks (stream order is enough).  All-or-nothing:
+ * PKV_ERR_OUT_OF_BLOCKS if the target pool is short, PKV_ERR_SWAPPED if a
+ * sequence is already in the other state, PKV_ERR_INVALID_ARG for a
+ * repeated id, no host pool, or more than max_pairs pairs.
+ *
+ * While a sequence is swapped out, append, copy-on-write append, fork (as
+ * source or destination), table building and the decode-step call refuse it
+ * with PKV_ERR_SWAPPED; pkv_seq_free releases its host blocks.
+ * ---------------------------------------------------------------------- */
+/* Gives the allocator its host pool (once; PKV_ERR_INVALID_ARG otherwise). */
+pkv_status pkv_allocator_set_host_pool(pkv_allocator* a, int32_t num_host_blocks,
+                                       const int32_t* host_free_order);
+pkv_status pkv_swap_out(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                        int64_t* pairs_out, int32_t max_pairs, int32_t* num_pairs_out);
+pkv_status pkv_swap_in(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                       int64_t* pairs_out, int32_t max_pairs, int32_t* num_pairs_out);
+/* 1 if swapped out, 0 if resident, -1 if unknown. */
+int32_t pkv_seq_is_swapped(const pkv_allocator* a, int64_t seq_id);
+/* Free host blocks, -1 without a host pool. */
+int32_t pkv_num_free_host_blocks(const pkv_allocator* a);
+/* Reference count of a host block (0 = free), -1 for an id outside the pool. */
+int32_t pkv_host_block_refcount(const pkv_allocator* a, int32_t host_block_id);
+
 int32_t pkv_num_free_blocks(const pkv_allocator* a);
 /* Reference count of a block (0 = free), -1 for an id outside the pool. */
 int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block_id);
 /* Length in tokens of a sequence, -1 if unknown. */
 int64_t pkv_seq_context_len(const pkv_allocator* a, int64_t seq_id);
-/* Number of blocks of a sequence, -1 if unknown. */
+/* Number of blocks of a sequence (device or host), -1 if unknown. */
 int32_t pkv_seq_num_blocks(const pkv_allocator* a, int64_t seq_id);
 
 #ifdef __cplusplus

@@ -20,6 +20,7 @@ __all__ = [
     "kv_reshape_and_cache", "paged_attention_decode", "decode_workspace_bytes",
     "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned", "longest_first_order",
     "paged_attention_prefill", "prefill_workspace_bytes", "prefill_partition_size",
+    "swap_blocks", "SWAP_OUT", "SWAP_IN",
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
 ]
 
@@ -33,8 +34,9 @@ PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 
 STATUS = {
     0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "OUT_OF_BLOCKS", -4: "NOT_FOUND",
-    -5: "SHARED_WRITE", -6: "WORKSPACE", -7: "HIP",
+    -5: "SHARED_WRITE", -6: "WORKSPACE", -7: "HIP", -8: "SWAPPED",
 }
+SWAP_OUT, SWAP_IN = 0, 1
 
 # name -> (restype, argtypes), the exported C ABI
 _i32, _i64, _sz, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
@@ -59,6 +61,14 @@ EXPORTS = {
     "pkv_get_decode_path": (_i32, []),
     "pkv_upload_pinned": (_i32, [_vp, _vp, _sz, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _vp]),
+    "pkv_allocator_set_host_pool": (_i32, [_vp, _i32, _P(_i32)]),
+    "pkv_swap_out": (_i32, [_vp, _P(_i64), _i32, _P(_i64), _i32, _P(_i32)]),
+    "pkv_swap_in": (_i32, [_vp, _P(_i64), _i32, _P(_i64), _i32, _P(_i32)]),
+    "pkv_seq_is_swapped": (_i32, [_vp, _i64]),
+    "pkv_num_free_host_blocks": (_i32, [_vp]),
+    "pkv_host_block_refcount": (_i32, [_vp, _i32]),
     "pkv_allocator_create": (_i32, [_i32, _i32, _P(_i32), _P(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
     "pkv_seq_add": (_i32, [_vp, _i64]),
@@ -245,6 +255,23 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
                                _stream_ptr(stream)), "copy_blocks")
 
 
+def swap_blocks(k_cache, v_cache, k_host, v_host, pairs, direction: int, stream=None) -> None:
+    """Swap copy between the device caches and the pinned host pools
+    ``[Nh, bs, Hkv, D]`` (torch CPU tensors from ``pin_memory()``):
+    SWAP_OUT copies device block ``src`` to host block ``dst`` for each row of
+    ``pairs`` (device int64 ``[P, 2]``), SWAP_IN host ``src`` to device ``dst``."""
+    N, bs, Hkv, D = k_cache.shape
+    Nh = k_host.shape[0]
+    if tuple(k_host.shape[1:]) != (bs, Hkv, D) or k_host.shape != v_host.shape:
+        raise ValueError("host pools must be [num_host_blocks, block_size, Hkv, D]")
+    if k_host.dtype != k_cache.dtype or v_host.dtype != k_cache.dtype:
+        raise TypeError("host pools must have the cache dtype")
+    _check(lib.pkv_swap_blocks(k_cache.data_ptr(), v_cache.data_ptr(), k_host.data_ptr(),
+                               v_host.data_ptr(), pairs.data_ptr(), pairs.shape[0], N, Nh, bs,
+                               Hkv, D, _dtype_code(k_cache), int(direction), _stream_ptr(stream)),
+           "swap_blocks")
+
+
 # ------------------------------------------------------------------ allocator
 class Allocator:
     """Host block allocator (C++); see ``pkv_allocator_*`` in ``include/pkv.h``."""
@@ -261,12 +288,13 @@ class Allocator:
         _check(lib.pkv_allocator_create(num_blocks, block_size, fo, ctypes.byref(h)),
                "allocator_create")
         self._h = h
+        self._destroy = lib.pkv_allocator_destroy  # still callable at interpreter exit
         self.num_blocks = num_blocks
         self.block_size = block_size
 
     def close(self) -> None:
         if getattr(self, "_h", None):
-            lib.pkv_allocator_destroy(self._h)
+            self._destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -316,6 +344,46 @@ class Allocator:
 
     def free(self, seq: int) -> None:
         _check(lib.pkv_seq_free(self._h, seq), "seq_free")
+
+    def set_host_pool(self, num_host_blocks: int,
+                      host_free_order: Optional[Sequence[int]] = None) -> None:
+        fo = None
+        if host_free_order is not None:
+            self._hfo = np.ascontiguousarray(host_free_order, dtype=np.int32)
+            if self._hfo.shape != (num_host_blocks,):
+                raise ValueError("host_free_order must have num_host_blocks entries")
+            fo = self._hfo.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        _check(lib.pkv_allocator_set_host_pool(self._h, num_host_blocks, fo), "set_host_pool")
+        self.num_host_blocks = num_host_blocks
+
+    def _move(self, fn, name: str, seqs: Sequence[int]) -> np.ndarray:
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        room = sum(max(self.num_blocks_of(int(x)), 0) for x in s)
+        pairs = np.empty((max(room, 1), 2), dtype=np.int64)
+        npairs = ctypes.c_int32(0)
+        _check(fn(self._h, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(s),
+                  pairs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(pairs),
+                  ctypes.byref(npairs)), name)
+        return pairs[: npairs.value].copy()
+
+    def swap_out(self, seqs: Sequence[int]) -> np.ndarray:
+        """Move the sequences to host blocks; returns the (device, host) block
+        pairs int64 [P, 2] to copy with ``swap_blocks(..., SWAP_OUT)``."""
+        return self._move(lib.pkv_swap_out, "swap_out", seqs)
+
+    def swap_in(self, seqs: Sequence[int]) -> np.ndarray:
+        """Move swapped-out sequences back to fresh device blocks; returns the
+        (host, device) pairs to copy with ``swap_blocks(..., SWAP_IN)``."""
+        return self._move(lib.pkv_swap_in, "swap_in", seqs)
+
+    def is_swapped(self, seq: int) -> int:
+        return int(lib.pkv_seq_is_swapped(self._h, seq))
+
+    def num_free_host_blocks(self) -> int:
+        return int(lib.pkv_num_free_host_blocks(self._h))
+
+    def host_block_refcount(self, block: int) -> int:
+        return int(lib.pkv_host_block_refcount(self._h, block))
 
     def build_block_tables(self, seqs: Sequence[int], max_blocks: int, pad: int = -1,
                            tables_out: Optional[np.ndarray] = None,

@@ -11,6 +11,10 @@
 // starts as the caller's free_order; a block whose count drops to zero joins
 // its tail.  Every operation checks all of its preconditions before changing
 // anything, so a failing call leaves the allocator as it was.
+//
+// Preemption by swapping ("What Is vLLM …", section "What is continuous
+// batching in vLLM?", step 2) moves a group of sequences between the device
+// pool and a second pool of blocks in host memory, managed the same way.
 #include <algorithm>
 #include <cstdint>
 #include <deque>
@@ -24,13 +28,21 @@
 
 struct pkv_allocator {
   struct Seq {
-    std::vector<int32_t> blocks;
+    std::vector<int32_t> blocks;  // device blocks, or host blocks while swapped
     int64_t len = 0;
+    bool swapped = false;
+  };
+  struct Pool {
+    std::deque<int32_t> free_q;
+    std::vector<int32_t> refcount;
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::deque<int32_t> free_q;
-  std::vector<int32_t> refcount;
+  Pool dev;   // the device cache's blocks
+  Pool host;  // the host pool's blocks (empty until set)
+  bool has_host = false;
+  std::deque<int32_t>& free_q = dev.free_q;
+  std::vector<int32_t>& refcount = dev.refcount;
   std::unordered_map<int64_t, Seq> seqs;
 
   int64_t blocks_for(int64_t tokens) const {
@@ -104,6 +116,9 @@ extern "C" pkv_status pkv_seq_fork_prefix(pkv_allocator* a, int64_t src, int64_t
   if (is == a->seqs.end() || id == a->seqs.end())
     return fail(PKV_ERR_NOT_FOUND, "seq_fork_prefix: unknown sequence (%lld -> %lld)",
                 (long long)src, (long long)dst);
+  if (is->second.swapped || id->second.swapped)
+    return fail(PKV_ERR_SWAPPED, "seq_fork_prefix: sequence %lld is swapped out",
+                (long long)(is->second.swapped ? src : dst));
   const auto& s = is->second;
   bool whole = num_tokens % a->block_size == 0 || num_tokens == s.len;
   if (src == dst || num_tokens < 0 || num_tokens > s.len || !whole || id->second.len != 0)
@@ -138,6 +153,8 @@ extern "C" pkv_status pkv_append_tokens(pkv_allocator* a, const int64_t* seq_ids
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end())
       return fail(PKV_ERR_NOT_FOUND, "append: unknown sequence %lld", (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_SWAPPED, "append: sequence %lld is swapped out", (long long)seq_ids[i]);
     if (num_tokens[i] < 0)
       return fail(PKV_ERR_INVALID_ARG, "append: negative token count %d", num_tokens[i]);
     const auto& s = it->second;
@@ -182,6 +199,9 @@ extern "C" pkv_status pkv_append_tokens_cow(pkv_allocator* a, const int64_t* seq
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end())
       return fail(PKV_ERR_NOT_FOUND, "append_cow: unknown sequence %lld", (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_SWAPPED, "append_cow: sequence %lld is swapped out",
+                  (long long)seq_ids[i]);
     if (num_tokens[i] < 0)
       return fail(PKV_ERR_INVALID_ARG, "append_cow: negative token count %d", num_tokens[i]);
     const auto& sq = it->second;
@@ -228,8 +248,9 @@ extern "C" pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id) {
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end())
     return fail(PKV_ERR_NOT_FOUND, "seq_free: unknown sequence %lld", (long long)seq_id);
+  auto& pool = it->second.swapped ? a->host : a->dev;
   for (int32_t b : it->second.blocks) {
-    if (--a->refcount[size_t(b)] == 0) a->free_q.push_back(b);
+    if (--pool.refcount[size_t(b)] == 0) pool.free_q.push_back(b);
   }
   a->seqs.erase(it);
   return pkv::ok();
@@ -248,6 +269,9 @@ extern "C" pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64
     if (it == a->seqs.end())
       return fail(PKV_ERR_NOT_FOUND, "build_block_tables: unknown sequence %lld",
                   (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_SWAPPED, "build_block_tables: sequence %lld is swapped out",
+                  (long long)seq_ids[i]);
     if (int64_t(it->second.blocks.size()) > max_blocks_per_seq)
       return fail(PKV_ERR_INVALID_ARG, "build_block_tables: sequence %lld has %zu blocks > %d",
                   (long long)seq_ids[i], it->second.blocks.size(), max_blocks_per_seq);
@@ -263,6 +287,127 @@ extern "C" pkv_status pkv_build_block_tables(const pkv_allocator* a, const int64
     if (context_lens_out) context_lens_out[i] = int32_t(s.len);
   }
   return pkv::ok();
+}
+
+extern "C" pkv_status pkv_allocator_set_host_pool(pkv_allocator* a, int32_t num_host_blocks,
+                                                  const int32_t* host_free_order) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "set_host_pool: NULL allocator");
+  if (a->has_host) return fail(PKV_ERR_INVALID_ARG, "set_host_pool: the host pool is already set");
+  if (num_host_blocks < 0)
+    return fail(PKV_ERR_INVALID_ARG, "set_host_pool: num_host_blocks=%d", num_host_blocks);
+  if (host_free_order) {
+    std::vector<char> seen(size_t(num_host_blocks), 0);
+    for (int32_t i = 0; i < num_host_blocks; ++i) {
+      const int32_t b = host_free_order[i];
+      if (b < 0 || b >= num_host_blocks || seen[size_t(b)])
+        return fail(PKV_ERR_INVALID_ARG,
+                    "set_host_pool: host_free_order is not a permutation (entry %d = %d)", i, b);
+      seen[size_t(b)] = 1;
+    }
+  }
+  a->host.refcount.assign(size_t(num_host_blocks), 0);
+  for (int32_t i = 0; i < num_host_blocks; ++i)
+    a->host.free_q.push_back(host_free_order ? host_free_order[i] : i);
+  a->has_host = true;
+  return pkv::ok();
+}
+
+namespace {
+
+// Moves a group of sequences from one pool to the other (swap-out: device to
+// host; swap-in: host to device).  Each distinct source block of the group
+// gets one destination block, taken from the destination pool's free queue
+// in visiting order (sequence by sequence, table order); every holder in the
+// group moves its reference, and a source block whose count drops to zero
+// rejoins its pool's free queue.  All preconditions are checked first.
+pkv_status move_group(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                      int64_t* pairs_out, int32_t max_pairs, int32_t* num_pairs_out,
+                      bool to_host) {
+  const char* what = to_host ? "swap_out" : "swap_in";
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "%s: NULL allocator", what);
+  if (!a->has_host) return fail(PKV_ERR_INVALID_ARG, "%s: the allocator has no host pool", what);
+  if (num_seqs < 0 || max_pairs < 0 || (num_seqs > 0 && !seq_ids) ||
+      (max_pairs > 0 && !pairs_out))
+    return fail(PKV_ERR_INVALID_ARG, "%s: bad arguments", what);
+  std::unordered_set<int64_t> seen;
+  for (int32_t i = 0; i < num_seqs; ++i)
+    if (!seen.insert(seq_ids[i]).second)
+      return fail(PKV_ERR_INVALID_ARG, "%s: sequence %lld listed twice", what,
+                  (long long)seq_ids[i]);
+  std::unordered_set<int32_t> distinct;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PKV_ERR_NOT_FOUND, "%s: unknown sequence %lld", what, (long long)seq_ids[i]);
+    if (it->second.swapped == to_host)
+      return fail(PKV_ERR_SWAPPED, "%s: sequence %lld is %s", what, (long long)seq_ids[i],
+                  to_host ? "already swapped out" : "not swapped out");
+    for (int32_t b : it->second.blocks) distinct.insert(b);
+  }
+  pkv_allocator::Pool& src = to_host ? a->dev : a->host;
+  pkv_allocator::Pool& dst = to_host ? a->host : a->dev;
+  const int64_t need = int64_t(distinct.size());
+  if (need > max_pairs)
+    return fail(PKV_ERR_INVALID_ARG, "%s: %lld block copies needed, room for %d", what,
+                (long long)need, max_pairs);
+  if (need > int64_t(dst.free_q.size()))
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "%s: need %lld %s blocks, %zu free", what,
+                (long long)need, to_host ? "host" : "device", dst.free_q.size());
+  std::unordered_map<int32_t, int32_t> moved;  // source block -> destination block
+  moved.reserve(size_t(need) * 2);
+  int32_t np = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto& sq = a->seqs[seq_ids[i]];
+    for (int32_t& b : sq.blocks) {
+      auto m = moved.find(b);
+      int32_t to;
+      if (m == moved.end()) {
+        to = dst.free_q.front();
+        dst.free_q.pop_front();
+        moved.emplace(b, to);
+        pairs_out[2 * np] = b;
+        pairs_out[2 * np + 1] = to;
+        ++np;
+      } else {
+        to = m->second;
+      }
+      dst.refcount[size_t(to)] += 1;
+      if (--src.refcount[size_t(b)] == 0) src.free_q.push_back(b);
+      b = to;
+    }
+    sq.swapped = to_host;
+  }
+  if (num_pairs_out) *num_pairs_out = np;
+  return pkv::ok();
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_swap_out(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                                   int64_t* pairs_out, int32_t max_pairs,
+                                   int32_t* num_pairs_out) {
+  return move_group(a, seq_ids, num_seqs, pairs_out, max_pairs, num_pairs_out, true);
+}
+
+extern "C" pkv_status pkv_swap_in(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                                  int64_t* pairs_out, int32_t max_pairs,
+                                  int32_t* num_pairs_out) {
+  return move_group(a, seq_ids, num_seqs, pairs_out, max_pairs, num_pairs_out, false);
+}
+
+extern "C" int32_t pkv_seq_is_swapped(const pkv_allocator* a, int64_t seq_id) {
+  if (!a) return -1;
+  auto it = a->seqs.find(seq_id);
+  return it == a->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
+}
+
+extern "C" int32_t pkv_num_free_host_blocks(const pkv_allocator* a) {
+  return a && a->has_host ? int32_t(a->host.free_q.size()) : -1;
+}
+
+extern "C" int32_t pkv_host_block_refcount(const pkv_allocator* a, int32_t host_block_id) {
+  if (!a || host_block_id < 0 || host_block_id >= int32_t(a->host.refcount.size())) return -1;
+  return a->host.refcount[size_t(host_block_id)];
 }
 
 extern "C" int32_t pkv_num_free_blocks(const pkv_allocator* a) {
@@ -305,6 +450,9 @@ extern "C" pkv_status pkv_decode_step_prepare(pkv_allocator* a, const int64_t* s
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end())
       return fail(PKV_ERR_NOT_FOUND, "decode_step_prepare: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_SWAPPED, "decode_step_prepare: sequence %lld is swapped out",
                   (long long)seq_ids[i]);
     if (a->blocks_for(it->second.len + 1) > max_blocks_per_seq)
       return fail(PKV_ERR_INVALID_ARG,
