@@ -49,6 +49,26 @@ mechanism; the reading here:
 * a swapped-out sequence cannot grow, fork or be listed in block tables
   until it is swapped in; freeing it releases its host blocks.
 
+Automatic prefix caching ("Serving models with vLLM", section "How it works:
+PagedAttention": requests with the same prefix, such as a system prompt, point
+at the same physical blocks, which is how prefix caching works; "What Is
+vLLM …", memory-sharing step: sequences whose KV caches are identical share
+blocks).  The pages give no mechanism; the reading here:
+
+* a full block's keys and values are fixed by the tokens of the whole prefix
+  that ends with it, so the cache maps that prefix (as a token tuple) to the
+  block holding it;
+* a new prompt shares the longest run of cached full blocks at its start,
+  but never its last token (its keys and values are computed, so the prompt
+  always has a query); a shared block that was free leaves the free list
+  (order of the others kept) and is held again;
+* the prompt's other full blocks are entered into the cache as they are
+  allocated (the caller writes their keys and values before any later
+  reader's attention runs); a key already present keeps its block;
+* a freed block keeps its entry until the free list hands it out for other
+  tokens; then its entry is dropped, and with it every entry whose prefix
+  extends it (they could only be reached through it).
+
 Token ``pos`` of a sequence is stored at slot ``table[pos // bs] * bs + pos % bs``.
 Test infrastructure only.
 """
@@ -117,6 +137,69 @@ class BlockAllocator:
         self.host_free: deque = deque()
         self.host_refcount: List[int] = []
         self.swapped: set = set()
+        # prefix cache (absent until enabled): whole-prefix token tuple -> block
+        self.prefix_cache: Optional[Dict[tuple, int]] = None
+        self.block_key: Dict[int, tuple] = {}
+        self.cache_lookups = 0
+        self.cache_hits = 0
+
+    def enable_prefix_cache(self) -> None:
+        if self.prefix_cache is not None:
+            raise InvalidArg("the prefix cache is already enabled")
+        self.prefix_cache = {}
+
+    def _take_free(self) -> int:
+        """Hand out the block at the head of the free list.  A block that still
+        held a cached prefix loses its entry, and so do the entries extending it."""
+        blk = self.free.popleft()
+        if self.prefix_cache is not None and blk in self.block_key:
+            key = self.block_key[blk]
+            for k in [k for k in self.prefix_cache if k[: len(key)] == key]:
+                del self.block_key[self.prefix_cache.pop(k)]
+        return blk
+
+    def add_prompt(self, seq: int, tokens: Sequence[int]) -> Tuple[List[int], int]:
+        """New sequence ``seq`` with prompt ``tokens``: shares the cached full
+        blocks of its longest cached prefix (never the last token), allocates
+        the rest, enters its other full blocks into the cache.  Returns the
+        slots of the tokens after the shared part and the number of shared
+        tokens."""
+        if seq in self.tables:
+            raise InvalidArg(f"sequence {seq} exists")
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        bs = self.block_size
+        hits: List[int] = []
+        if self.prefix_cache is not None:
+            for j in range(max(n - 1, 0) // bs):
+                blk = self.prefix_cache.get(tuple(tokens[: (j + 1) * bs]))
+                if blk is None:
+                    break
+                hits.append(blk)
+        revived = sum(1 for b in hits if self.refcount[b] == 0)
+        need = blocks_for(n, bs) - len(hits)
+        if need > len(self.free) - revived:
+            raise OutOfBlocks(f"need {need} blocks, {len(self.free) - revived} free")
+        for b in hits:
+            if self.refcount[b] == 0:
+                self.free.remove(b)
+            self.refcount[b] += 1
+        self.tables[seq] = list(hits)
+        self.lengths[seq] = len(hits) * bs
+        slots = self.append(seq, n - len(hits) * bs)
+        if self.prefix_cache is not None:
+            self.cache_lookups += max(n - 1, 0) // bs
+            self.cache_hits += len(hits)
+            for j in range(len(hits), n // bs):
+                key = tuple(tokens[: (j + 1) * bs])
+                if key not in self.prefix_cache:
+                    self.prefix_cache[key] = self.tables[seq][j]
+                    self.block_key[self.tables[seq][j]] = key
+        return slots, len(hits) * bs
+
+    def prefix_cache_stats(self) -> Tuple[int, int, int]:
+        """(full-block lookups, hits, blocks holding a cached prefix)."""
+        return self.cache_lookups, self.cache_hits, len(self.prefix_cache or {})
 
     def set_host_pool(self, num_host_blocks: int,
                       host_free_order: Optional[Iterable[int]] = None) -> None:
@@ -180,7 +263,7 @@ class BlockAllocator:
         slots = []
         for pos in range(length, length + n):
             if pos % bs == 0:
-                blk = self.free.popleft()
+                blk = self._take_free()
                 self.refcount[blk] += 1
                 table.append(blk)
             slots.append(slot_of(table, pos, bs))
@@ -203,7 +286,7 @@ class BlockAllocator:
         pairs = []
         if copy:
             old = table[-1]
-            new = self.free.popleft()
+            new = self._take_free()
             self.refcount[new] += 1
             self.refcount[old] -= 1
             table[-1] = new
@@ -291,7 +374,7 @@ class BlockAllocator:
             new_table = []
             for blk in self.tables[s]:
                 if blk not in to_dev:
-                    to_dev[blk] = self.free.popleft()
+                    to_dev[blk] = self._take_free()
                     pairs.append((blk, to_dev[blk]))
                 self.refcount[to_dev[blk]] += 1
                 self.host_refcount[blk] -= 1

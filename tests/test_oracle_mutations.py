@@ -11,6 +11,7 @@ import pytest
 import test_oracle_allocator as TAL
 import test_oracle_attention as TA
 import test_oracle_cache_write as TC
+import test_oracle_prefix_cache as TPC
 import test_oracle_swap as TS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -78,7 +79,7 @@ ALLOC = [
     ("return (num_tokens + block_size - 1) // block_size", "return num_tokens // block_size"),
     ("return int(table[pos // block_size]) * block_size + pos % block_size",
      "return int(table[pos // block_size]) * block_size + pos // block_size"),
-    ("blk = self.free.popleft()", "blk = self.free.pop()"),
+    ("        blk = self.free.popleft()\n", "        blk = self.free.pop()\n"),
     ("self.free.append(blk)", "self.free.appendleft(blk)"),
     ("if pos % bs == 0:", "if pos % bs == 1:"),
     ("self.refcount[blk] -= 1", "self.refcount[blk] -= 2"),
@@ -109,7 +110,7 @@ def test_allocator_mutant_caught(old, new, monkeypatch):
 SWAP_ALLOC = [
     ("                if blk not in to_host:\n", "                if True:\n"),
     ("to_host[blk] = self.host_free.popleft()", "to_host[blk] = self.host_free.pop()"),
-    ("to_dev[blk] = self.free.popleft()", "to_dev[blk] = self.free.pop()"),
+    ("to_dev[blk] = self._take_free()", "to_dev[blk] = self.free.pop()"),
     ("                self.refcount[blk] -= 1\n                if self.refcount[blk] == 0:\n"
      "                    self.free.append(blk)\n                new_table.append(to_host[blk])",
      "                self.refcount[blk] -= 1\n                new_table.append(to_host[blk])"),
@@ -143,3 +144,36 @@ SWAP_MOVE = [
 def test_swap_move_mutant_caught(old, new, monkeypatch):
     monkeypatch.setattr(TS, "OC", _mutant("oracle/cache_write.py", old, new))
     assert _caught(TS.PINS)
+
+
+PREFIX = [
+    # the key is the block's own tokens, not the whole prefix
+    ("blk = self.prefix_cache.get(tuple(tokens[: (j + 1) * bs]))",
+     "blk = self.prefix_cache.get(tuple(tokens[j * bs: (j + 1) * bs]))"),
+    ("                key = tuple(tokens[: (j + 1) * bs])\n",
+     "                key = tuple(tokens[j * bs: (j + 1) * bs])\n"),
+    # the last prompt token may be shared
+    ("            for j in range(max(n - 1, 0) // bs):", "            for j in range(n // bs):"),
+    # a revived block stays in the free list
+    ("                self.free.remove(b)\n", "                pass\n"),
+    # revived blocks are not counted against the free list
+    ("need > len(self.free) - revived:", "need > len(self.free):"),
+    # the entries extending an evicted block survive
+    ("for k in [k for k in self.prefix_cache if k[: len(key)] == key]:",
+     "for k in [k for k in self.prefix_cache if k == key]:"),
+    # a handed-out block keeps its entry
+    ("        if self.prefix_cache is not None and blk in self.block_key:\n",
+     "        if False:\n"),
+    # an existing entry is replaced by the new block
+    ("                if key not in self.prefix_cache:\n", "                if True:\n"),
+    # the partial last block is entered too
+    ("            for j in range(len(hits), n // bs):", "            for j in range(len(hits), blocks_for(n, bs)):"),
+    # hits are not counted
+    ("            self.cache_hits += len(hits)\n", "\n"),
+]
+
+
+@pytest.mark.parametrize("old,new", PREFIX, ids=[f"prefix{i}" for i in range(len(PREFIX))])
+def test_prefix_cache_mutant_caught(old, new, monkeypatch):
+    monkeypatch.setattr(TPC, "OAL", _mutant("oracle/allocator.py", old, new))
+    assert _caught(TPC.PINS)
