@@ -47,6 +47,9 @@ def _args():
     ap.add_argument("--staging-depth", type=int, default=8,
                     help="pinned staging buffers in flight (steps the host may run ahead)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
+    ap.add_argument("--prefix-cache", action="store_true",
+                    help="measure admitting requests that share a cached 2,000-token system "
+                         "prompt, against the same requests computed in full")
     ap.add_argument("--swap", action="store_true",
                     help="measure preemption swapping instead: a quarter of the sequences "
                          "swapped out to pinned host memory and back, per step")
@@ -319,6 +322,104 @@ def run_swap(args) -> int:
     return 0
 
 
+def run_prefix_cache(args) -> int:
+    """Admission of a batch of new requests that share a 2,000-token system
+    prompt (16 requests of 2,000 + 512 tokens; LLaMA-13B attention shape: 40
+    heads of 128, bf16, blocks of 16).  A step: the host allocator admits the
+    batch (add_prompt), the tables and slots are uploaded, the cache write
+    stores the computed tokens' K/V and chunked prefill runs their queries
+    over the whole prompt; the batch is then freed (untimed).  With the prefix
+    cache the system prompt's blocks stay cached between steps and only each
+    request's own 512 tokens are computed; without it every token is."""
+    import torch
+    import paged_kv_cache_292_amd as P
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Hq, Hkv, D, bs, sys_len, own = 16, 40, 40, 128, 16, 2000, 512
+    rng = np.random.default_rng(20)
+    system = rng.integers(0, 32000, size=sys_len).astype(np.int32)
+    L = sys_len + own
+    # fresh own tokens for every request of every step (only the system
+    # prompt repeats); the same prompts for both runs
+    total = args.warmup + args.steps
+    own_tokens = rng.integers(0, 32000, size=(total, B, own)).astype(np.int32)
+    N = B * (-(-L // bs)) + 64
+    k_cache = torch.randn((N, bs, Hkv, D), device=dev).to(torch.bfloat16)
+    v_cache = torch.randn((N, bs, Hkv, D), device=dev).to(torch.bfloat16)
+    new_k = torch.randn((B * L, Hkv, D), device=dev).to(torch.bfloat16)
+    new_v = torch.randn((B * L, Hkv, D), device=dev).to(torch.bfloat16)
+    q = torch.randn((B * L, Hq, D), device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for share in (True, False):
+        alloc = P.Allocator(N, bs)
+        if share:
+            alloc.enable_prefix_cache()
+            alloc.add_prompt(10_000, system)  # the system prompt computed once, earlier
+            alloc.free(10_000)                # its blocks stay cached in the free list
+        mb = -(-L // bs) + 1
+        slots = np.empty(B * L, dtype=np.int64)
+        times, dev_times, computed = [], [], []
+        for it in range(args.warmup + args.steps):
+            prompts = [np.concatenate([system, own_tokens[it, i]]) for i in range(B)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            n_slots, counts = 0, []
+            for i, pr in enumerate(prompts):
+                sl, c = alloc.add_prompt(i, pr, slots_out=slots[n_slots:])
+                counts.append(L - c)
+                n_slots += len(sl)
+            tables, ctx = alloc.build_block_tables(list(range(B)), mb)
+            starts = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+            d_slots = torch.from_numpy(slots[:n_slots]).to(dev, non_blocking=False)
+            d_tab = torch.from_numpy(tables).to(dev)
+            d_ctx = torch.from_numpy(ctx).to(dev)
+            d_st = torch.from_numpy(starts).to(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            P.kv_reshape_and_cache(new_k[:n_slots], new_v[:n_slots], k_cache, v_cache, d_slots)
+            T = int(starts[-1])
+            P.paged_attention_prefill(out[:T], q[:T], d_st, max(counts), k_cache, v_cache, d_tab,
+                                      d_ctx, L, 1.0 / np.sqrt(D), 0, None)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for i in range(B):
+                alloc.free(i)
+            if it >= args.warmup:
+                times.append(t1 - t0)
+                dev_times.append(e0.elapsed_time(e1) * 1e-3)
+                computed.append(T)
+        key = "with_prefix_cache" if share else "without_prefix_cache"
+        step = float(np.mean(times))
+        res[key] = {"step_ms": round(step * 1e3, 3),
+                    "device_ms": round(float(np.mean(dev_times)) * 1e3, 3),
+                    "computed_tokens_per_step": int(np.mean(computed)),
+                    "prompt_tokens_per_s": round(B * L / step, 1),
+                    "requests_per_s": round(B / step, 1)}
+        if share:
+            lk, ht, nc = alloc.prefix_cache_stats()
+            res[key]["block_hit_rate"] = round(ht / max(lk, 1), 4)
+        alloc.close()
+    w, wo = res["with_prefix_cache"], res["without_prefix_cache"]
+    line = {
+        "metric": "prompt admission with a shared 2,000-token system prompt: prompt tokens/s",
+        "value": w["prompt_tokens_per_s"], "unit": "prompt tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": w["step_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random tokens, K/V and queries)",
+        "config": {"workload": "shared_system_prompt_bf16", "num_requests": B,
+                   "system_prompt_tokens": sys_len, "own_tokens": own, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": bs},
+        "with_prefix_cache": w, "without_prefix_cache": wo,
+        "speedup": round(wo["step_ms"] / w["step_ms"], 2),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     args = _args()
     if args.summarize_profile:
@@ -331,6 +432,8 @@ def main() -> int:
         return 2
     if args.swap:
         return run_swap(args)
+    if args.prefix_cache:
+        return run_prefix_cache(args)
     import torch
     import paged_kv_cache_292_amd as P
     import workloads as W

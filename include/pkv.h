@@ -418,6 +418,35 @@ int32_t pkv_num_free_host_blocks(const pkv_allocator* a);
 /* Reference count of a host block (0 = free), -1 for an id outside the pool. */
 int32_t pkv_host_block_refcount(const pkv_allocator* a, int32_t host_block_id);
 
+/* ------------------------------------------------------------------------
+ * Automatic prefix caching: requests with the same prefix (a system prompt,
+ * a document) point at the same physical blocks ("Serving models with vLLM",
+ * section "How it works: PagedAttention"; "What Is vLLM …", memory-sharing
+ * step).  With the cache enabled, a full block is entered under the tokens
+ * of the whole prefix it ends.  pkv_seq_add_prompt creates sequence seq_id
+ * for a prompt (host int32 tokens [num_tokens]): it shares the longest run
+ * of cached full blocks at the prompt's start, but never the block holding
+ * the last token (that token is always computed), allocates the rest and
+ * enters the prompt's other full blocks.  slots_out (host int64, [num_tokens
+ * - cached]) receives the slots of the tokens after the shared part and
+ * *num_cached_out the shared token count: the caller writes only those
+ * tokens' K/V (pkv_kv_reshape_and_cache) before any later reader's attention
+ * runs, and runs prefill for them over the whole context.  A freed block
+ * keeps its entry (and can be shared again, leaving the free list with the
+ * others' order kept) until the free list hands it out for other tokens;
+ * then its entry and every entry extending it are dropped.  Without the
+ * cache enabled the call is seq_add + append.  All-or-nothing:
+ * PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_INVALID_ARG (the id exists).
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_allocator_enable_prefix_cache(pkv_allocator* a);
+pkv_status pkv_seq_add_prompt(pkv_allocator* a, int64_t seq_id, const int32_t* tokens,
+                              int32_t num_tokens, int64_t* slots_out,
+                              int32_t* num_cached_out);
+/* Full-block lookups and hits so far (the cache hit rate is hits / lookups)
+ * and the number of blocks holding a cached prefix; any pointer may be NULL. */
+pkv_status pkv_prefix_cache_stats(const pkv_allocator* a, int64_t* lookups, int64_t* hits,
+                                  int32_t* num_cached_blocks);
+
 int32_t pkv_num_free_blocks(const pkv_allocator* a);
 /* Reference count of a block (0 = free), -1 for an id outside the pool. */
 int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block_id);

@@ -67,6 +67,9 @@ EXPORTS = {
     "pkv_swap_out": (_i32, [_vp, _P(_i64), _i32, _P(_i64), _i32, _P(_i32)]),
     "pkv_swap_in": (_i32, [_vp, _P(_i64), _i32, _P(_i64), _i32, _P(_i32)]),
     "pkv_seq_is_swapped": (_i32, [_vp, _i64]),
+    "pkv_allocator_enable_prefix_cache": (_i32, [_vp]),
+    "pkv_seq_add_prompt": (_i32, [_vp, _i64, _P(_i32), _i32, _P(_i64), _P(_i32)]),
+    "pkv_prefix_cache_stats": (_i32, [_vp, _P(_i64), _P(_i64), _P(_i32)]),
     "pkv_num_free_host_blocks": (_i32, [_vp]),
     "pkv_host_block_refcount": (_i32, [_vp, _i32]),
     "pkv_allocator_create": (_i32, [_i32, _i32, _P(_i32), _P(_vp)]),
@@ -375,6 +378,30 @@ class Allocator:
         """Move swapped-out sequences back to fresh device blocks; returns the
         (host, device) pairs to copy with ``swap_blocks(..., SWAP_IN)``."""
         return self._move(lib.pkv_swap_in, "swap_in", seqs)
+
+    def enable_prefix_cache(self) -> None:
+        _check(lib.pkv_allocator_enable_prefix_cache(self._h), "enable_prefix_cache")
+
+    def add_prompt(self, seq: int, tokens: Sequence[int],
+                   slots_out: Optional[np.ndarray] = None) -> Tuple[np.ndarray, int]:
+        """New sequence for a prompt; returns (slots of the tokens after the
+        shared cached prefix, number of shared tokens)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        out = slots_out if slots_out is not None else np.empty(len(t), dtype=np.int64)
+        if out.dtype != np.int64 or out.size < len(t) or not out.flags.c_contiguous:
+            raise ValueError("slots_out must be a contiguous int64 array of len(tokens)")
+        cached = ctypes.c_int32(0)
+        _check(lib.pkv_seq_add_prompt(self._h, seq, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      len(t), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                      ctypes.byref(cached)), "seq_add_prompt")
+        return out[: len(t) - cached.value], int(cached.value)
+
+    def prefix_cache_stats(self) -> Tuple[int, int, int]:
+        """(full-block lookups, hits, blocks holding a cached prefix)."""
+        lk, ht, nc = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+        _check(lib.pkv_prefix_cache_stats(self._h, ctypes.byref(lk), ctypes.byref(ht),
+                                          ctypes.byref(nc)), "prefix_cache_stats")
+        return int(lk.value), int(ht.value), int(nc.value)
 
     def is_swapped(self, seq: int) -> int:
         return int(lib.pkv_seq_is_swapped(self._h, seq))

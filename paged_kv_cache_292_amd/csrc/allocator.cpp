@@ -26,24 +26,96 @@
 
 #include "pkv_internal.h"
 
+namespace {
+
+// Free list of one pool: first-in first-out, and a free block can also be
+// taken out of the middle (a cached block shared again) without disturbing
+// the order of the others.  Entries are (block, stamp); a block's current
+// stamp is set when it is freed and cleared when it is taken, so entries
+// left behind by a take are recognised as stale and skipped.
+struct Pool {
+  std::deque<std::pair<int32_t, uint64_t>> q;
+  std::vector<uint64_t> stamp;  // 0 = held
+  std::vector<int32_t> refcount;
+  uint64_t next_stamp = 1;
+  int64_t nfree = 0;
+
+  void init(int32_t n, const int32_t* order) {
+    stamp.assign(size_t(n), 0);
+    refcount.assign(size_t(n), 0);
+    for (int32_t i = 0; i < n; ++i) push(order ? order[i] : i);
+  }
+  int64_t size() const { return nfree; }
+  bool is_free(int32_t b) const { return stamp[size_t(b)] != 0; }
+  void push(int32_t b) {
+    stamp[size_t(b)] = next_stamp++;
+    q.emplace_back(b, stamp[size_t(b)]);
+    ++nfree;
+  }
+  int32_t pop() {  // the head; the caller checked size() > 0
+    while (q.front().second != stamp[size_t(q.front().first)]) q.pop_front();
+    const int32_t b = q.front().first;
+    q.pop_front();
+    stamp[size_t(b)] = 0;
+    --nfree;
+    return b;
+  }
+  void take(int32_t b) {  // out of the middle
+    stamp[size_t(b)] = 0;
+    --nfree;
+    if (q.size() > size_t(2 * nfree + 64)) {  // drop the stale entries
+      std::deque<std::pair<int32_t, uint64_t>> keep;
+      for (const auto& e : q)
+        if (e.second == stamp[size_t(e.first)]) keep.push_back(e);
+      q.swap(keep);
+    }
+  }
+};
+
+// Prefix-cache key of a full block: the block cached for the prefix before
+// it (-1 for the first block) and the block's own tokens.  Because an
+// entry is dropped together with every entry below it, a parent id always
+// names the same prefix, so the key names the whole prefix exactly.
+struct CacheKey {
+  int32_t parent = -1;
+  std::vector<int32_t> tokens;
+  bool operator==(const CacheKey& o) const { return parent == o.parent && tokens == o.tokens; }
+};
+struct CacheKeyHash {
+  size_t operator()(const CacheKey& k) const {
+    uint64_t h = 0x9E3779B97F4A7C15ull ^ uint64_t(uint32_t(k.parent));
+    for (int32_t t : k.tokens) {
+      h ^= uint64_t(uint32_t(t)) + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+      h *= 0xBF58476D1CE4E5B9ull;
+    }
+    return size_t(h ^ (h >> 31));
+  }
+};
+
+}  // namespace
+
 struct pkv_allocator {
   struct Seq {
     std::vector<int32_t> blocks;  // device blocks, or host blocks while swapped
     int64_t len = 0;
     bool swapped = false;
   };
-  struct Pool {
-    std::deque<int32_t> free_q;
-    std::vector<int32_t> refcount;
-  };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
   Pool dev;   // the device cache's blocks
   Pool host;  // the host pool's blocks (empty until set)
   bool has_host = false;
-  std::deque<int32_t>& free_q = dev.free_q;
   std::vector<int32_t>& refcount = dev.refcount;
   std::unordered_map<int64_t, Seq> seqs;
+
+  // prefix cache (off until enabled)
+  bool cache_on = false;
+  std::unordered_map<CacheKey, int32_t, CacheKeyHash> cache;
+  std::vector<CacheKey> block_key;               // valid where block_cached
+  std::vector<char> block_cached;
+  std::vector<std::vector<int32_t>> children;    // cached blocks keyed under this one
+  int64_t lookups = 0;
+  int64_t hits = 0;
 
   int64_t blocks_for(int64_t tokens) const {
     return (tokens + block_size - 1) / block_size;
@@ -53,12 +125,37 @@ struct pkv_allocator {
   bool writes_shared(const Seq& s, int64_t n) const {
     return n > 0 && s.len % block_size != 0 && refcount[s.blocks.back()] > 1;
   }
+  // Drops block b's cache entry and every entry below it.
+  void evict(int32_t b) {
+    std::vector<int32_t> stack{b};
+    while (!stack.empty()) {
+      const int32_t x = stack.back();
+      stack.pop_back();
+      if (!block_cached[size_t(x)]) continue;
+      const int32_t parent = block_key[size_t(x)].parent;
+      if (parent >= 0) {
+        auto& sib = children[size_t(parent)];
+        sib.erase(std::remove(sib.begin(), sib.end(), x), sib.end());
+      }
+      cache.erase(block_key[size_t(x)]);
+      block_key[size_t(x)] = CacheKey{};
+      block_cached[size_t(x)] = 0;
+      for (int32_t c : children[size_t(x)]) stack.push_back(c);
+      children[size_t(x)].clear();
+    }
+  }
+  // Hands out the device free list's head; a block that still held a cached
+  // prefix is about to receive other tokens and loses its entry.
+  int32_t take_free() {
+    const int32_t b = dev.pop();
+    if (cache_on && block_cached[size_t(b)]) evict(b);
+    return b;
+  }
   // Appends n tokens (preconditions already checked), writing slots.
   void grow(Seq& s, int64_t n, int64_t* slots) {
     for (int64_t pos = s.len; pos < s.len + n; ++pos) {
       if (pos % block_size == 0) {
-        int32_t blk = free_q.front();
-        free_q.pop_front();
+        int32_t blk = take_free();
         refcount[blk] += 1;
         s.blocks.push_back(blk);
       }
@@ -93,8 +190,7 @@ extern "C" pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_siz
   if (!a) return fail(PKV_ERR_INVALID_ARG, "allocator_create: out of host memory");
   a->num_blocks = num_blocks;
   a->block_size = block_size;
-  a->refcount.assign(size_t(num_blocks), 0);
-  for (int32_t i = 0; i < num_blocks; ++i) a->free_q.push_back(free_order ? free_order[i] : i);
+  a->dev.init(num_blocks, free_order);
   *out = a;
   return pkv::ok();
 }
@@ -167,9 +263,9 @@ extern "C" pkv_status pkv_append_tokens(pkv_allocator* a, const int64_t* seq_ids
     need += a->blocks_for(before + num_tokens[i]) - a->blocks_for(before);
     extra += num_tokens[i];
   }
-  if (need > int64_t(a->free_q.size()))
-    return fail(PKV_ERR_OUT_OF_BLOCKS, "append: need %lld blocks, %zu free", (long long)need,
-                a->free_q.size());
+  if (need > a->dev.size())
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "append: need %lld blocks, %lld free", (long long)need,
+                (long long)a->dev.size());
   int64_t* out = slots_out;
   for (int32_t i = 0; i < num_seqs; ++i) {
     a->grow(a->seqs[seq_ids[i]], num_tokens[i], out);
@@ -218,17 +314,16 @@ extern "C" pkv_status pkv_append_tokens_cow(pkv_allocator* a, const int64_t* seq
   if (pairs > max_pairs)
     return fail(PKV_ERR_INVALID_ARG, "append_cow: %d copies needed, room for %d", pairs,
                 max_pairs);
-  if (need > int64_t(a->free_q.size()))
-    return fail(PKV_ERR_OUT_OF_BLOCKS, "append_cow: need %lld blocks, %zu free",
-                (long long)need, a->free_q.size());
+  if (need > a->dev.size())
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "append_cow: need %lld blocks, %lld free",
+                (long long)need, (long long)a->dev.size());
   int32_t np = 0;
   int64_t* out = slots_out;
   for (int32_t i = 0; i < num_seqs; ++i) {
     auto& sq = a->seqs[seq_ids[i]];
     if (a->writes_shared(sq, num_tokens[i])) {
       const int32_t old = sq.blocks.back();
-      const int32_t fresh = a->free_q.front();
-      a->free_q.pop_front();
+      const int32_t fresh = a->take_free();
       a->refcount[size_t(fresh)] += 1;
       a->refcount[size_t(old)] -= 1;  // still > 0: another sequence holds it
       sq.blocks.back() = fresh;
@@ -250,7 +345,7 @@ extern "C" pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id) {
     return fail(PKV_ERR_NOT_FOUND, "seq_free: unknown sequence %lld", (long long)seq_id);
   auto& pool = it->second.swapped ? a->host : a->dev;
   for (int32_t b : it->second.blocks) {
-    if (--pool.refcount[size_t(b)] == 0) pool.free_q.push_back(b);
+    if (--pool.refcount[size_t(b)] == 0) pool.push(b);
   }
   a->seqs.erase(it);
   return pkv::ok();
@@ -305,9 +400,7 @@ extern "C" pkv_status pkv_allocator_set_host_pool(pkv_allocator* a, int32_t num_
       seen[size_t(b)] = 1;
     }
   }
-  a->host.refcount.assign(size_t(num_host_blocks), 0);
-  for (int32_t i = 0; i < num_host_blocks; ++i)
-    a->host.free_q.push_back(host_free_order ? host_free_order[i] : i);
+  a->host.init(num_host_blocks, host_free_order);
   a->has_host = true;
   return pkv::ok();
 }
@@ -344,15 +437,15 @@ pkv_status move_group(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs
                   to_host ? "already swapped out" : "not swapped out");
     for (int32_t b : it->second.blocks) distinct.insert(b);
   }
-  pkv_allocator::Pool& src = to_host ? a->dev : a->host;
-  pkv_allocator::Pool& dst = to_host ? a->host : a->dev;
+  Pool& src = to_host ? a->dev : a->host;
+  Pool& dst = to_host ? a->host : a->dev;
   const int64_t need = int64_t(distinct.size());
   if (need > max_pairs)
     return fail(PKV_ERR_INVALID_ARG, "%s: %lld block copies needed, room for %d", what,
                 (long long)need, max_pairs);
-  if (need > int64_t(dst.free_q.size()))
-    return fail(PKV_ERR_OUT_OF_BLOCKS, "%s: need %lld %s blocks, %zu free", what,
-                (long long)need, to_host ? "host" : "device", dst.free_q.size());
+  if (need > dst.size())
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "%s: need %lld %s blocks, %lld free", what,
+                (long long)need, to_host ? "host" : "device", (long long)dst.size());
   std::unordered_map<int32_t, int32_t> moved;  // source block -> destination block
   moved.reserve(size_t(need) * 2);
   int32_t np = 0;
@@ -362,8 +455,7 @@ pkv_status move_group(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs
       auto m = moved.find(b);
       int32_t to;
       if (m == moved.end()) {
-        to = dst.free_q.front();
-        dst.free_q.pop_front();
+        to = to_host ? dst.pop() : a->take_free();
         moved.emplace(b, to);
         pairs_out[2 * np] = b;
         pairs_out[2 * np + 1] = to;
@@ -372,7 +464,7 @@ pkv_status move_group(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs
         to = m->second;
       }
       dst.refcount[size_t(to)] += 1;
-      if (--src.refcount[size_t(b)] == 0) src.free_q.push_back(b);
+      if (--src.refcount[size_t(b)] == 0) src.push(b);
       b = to;
     }
     sq.swapped = to_host;
@@ -402,7 +494,7 @@ extern "C" int32_t pkv_seq_is_swapped(const pkv_allocator* a, int64_t seq_id) {
 }
 
 extern "C" int32_t pkv_num_free_host_blocks(const pkv_allocator* a) {
-  return a && a->has_host ? int32_t(a->host.free_q.size()) : -1;
+  return a && a->has_host ? int32_t(a->host.size()) : -1;
 }
 
 extern "C" int32_t pkv_host_block_refcount(const pkv_allocator* a, int32_t host_block_id) {
@@ -410,8 +502,85 @@ extern "C" int32_t pkv_host_block_refcount(const pkv_allocator* a, int32_t host_
   return a->host.refcount[size_t(host_block_id)];
 }
 
+extern "C" pkv_status pkv_allocator_enable_prefix_cache(pkv_allocator* a) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "enable_prefix_cache: NULL allocator");
+  if (a->cache_on) return fail(PKV_ERR_INVALID_ARG, "enable_prefix_cache: already enabled");
+  a->cache_on = true;
+  a->block_key.assign(size_t(a->num_blocks), CacheKey{});
+  a->block_cached.assign(size_t(a->num_blocks), 0);
+  a->children.assign(size_t(a->num_blocks), {});
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_seq_add_prompt(pkv_allocator* a, int64_t seq_id, const int32_t* tokens,
+                                         int32_t num_tokens, int64_t* slots_out,
+                                         int32_t* num_cached_out) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "seq_add_prompt: NULL allocator");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens))
+    return fail(PKV_ERR_INVALID_ARG, "seq_add_prompt: bad prompt (num_tokens=%d)", num_tokens);
+  if (a->seqs.count(seq_id))
+    return fail(PKV_ERR_INVALID_ARG, "seq_add_prompt: sequence %lld exists", (long long)seq_id);
+  const int64_t n = num_tokens;
+  const int64_t bs = a->block_size;
+  // the longest cached run of full blocks at the start, never the last token
+  std::vector<int32_t> hit;
+  CacheKey key;
+  if (a->cache_on) {
+    key.tokens.resize(size_t(bs));
+    for (int64_t j = 0; j < (n > 0 ? (n - 1) / bs : 0); ++j) {
+      std::copy(tokens + j * bs, tokens + (j + 1) * bs, key.tokens.begin());
+      auto it = a->cache.find(key);
+      if (it == a->cache.end()) break;
+      hit.push_back(it->second);
+      key.parent = it->second;
+    }
+  }
+  int64_t revived = 0;
+  for (int32_t b : hit) revived += a->dev.is_free(b) ? 1 : 0;
+  const int64_t need = a->blocks_for(n) - int64_t(hit.size());
+  if (need > a->dev.size() - revived)
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "seq_add_prompt: need %lld blocks, %lld free",
+                (long long)need, (long long)(a->dev.size() - revived));
+  for (int32_t b : hit) {
+    if (a->dev.is_free(b)) a->dev.take(b);
+    a->refcount[size_t(b)] += 1;
+  }
+  auto& sq = a->seqs[seq_id];
+  sq.blocks = hit;
+  sq.len = int64_t(hit.size()) * bs;
+  a->grow(sq, n - sq.len, slots_out);
+  if (a->cache_on) {
+    a->lookups += n > 0 ? (n - 1) / bs : 0;
+    a->hits += int64_t(hit.size());
+    key.parent = hit.empty() ? -1 : hit.back();
+    for (int64_t j = int64_t(hit.size()); j < n / bs; ++j) {
+      std::copy(tokens + j * bs, tokens + (j + 1) * bs, key.tokens.begin());
+      auto it = a->cache.find(key);
+      if (it == a->cache.end()) {  // enter the block; an existing entry keeps its block
+        const int32_t b = sq.blocks[size_t(j)];
+        it = a->cache.emplace(key, b).first;
+        a->block_key[size_t(b)] = key;
+        a->block_cached[size_t(b)] = 1;
+        if (key.parent >= 0) a->children[size_t(key.parent)].push_back(b);
+      }
+      key.parent = it->second;
+    }
+  }
+  if (num_cached_out) *num_cached_out = int32_t(hit.size() * size_t(bs));
+  return pkv::ok();
+}
+
+extern "C" pkv_status pkv_prefix_cache_stats(const pkv_allocator* a, int64_t* lookups,
+                                             int64_t* hits, int32_t* num_cached_blocks) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "prefix_cache_stats: NULL allocator");
+  if (lookups) *lookups = a->lookups;
+  if (hits) *hits = a->hits;
+  if (num_cached_blocks) *num_cached_blocks = int32_t(a->cache.size());
+  return pkv::ok();
+}
+
 extern "C" int32_t pkv_num_free_blocks(const pkv_allocator* a) {
-  return a ? int32_t(a->free_q.size()) : -1;
+  return a ? int32_t(a->dev.size()) : -1;
 }
 
 extern "C" int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block_id) {
