@@ -106,7 +106,10 @@ pkv_status pkv_kv_reshape_and_cache(const void* key, const void* value,
  * many tokens, handled in parallel, then merged by a log-sum-exp reduction;
  * the result equals the single-pass one up to rounding.
  * partition_size == 0: single pass per sequence.
- * partition_size == PKV_PARTITION_AUTO (-1): the library chooses.
+ * partition_size == PKV_PARTITION_AUTO (-1): the library chooses from
+ * max_context_len and the kernel that runs (pkv_decode_partition_size tells
+ * the choice; the decode-path setting must be the same when sizing the
+ * workspace and when calling).
  *
  * out           device, [num_seqs, num_q_heads, head_dim].
  * q             device, [num_seqs, num_q_heads, head_dim].

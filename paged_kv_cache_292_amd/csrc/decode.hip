@@ -8,11 +8,13 @@
 // [num_kv_heads][head_dim]; one token's row of one kv head is head_dim
 // contiguous elements.
 //
-// Work split.  A workgroup owns (sequence, kv head, partition).  Its waves
-// take 16-token chunks of the partition round-robin; inside a wave the four
-// 16-lane rows each own one token slot of the chunk and every lane holds
-// head_dim/16 elements of a row, so one 16-byte load per lane fetches four
-// token rows (4 x 256 B for bf16, head_dim 128).  q·k is summed over the 16
+// Work split.  A workgroup owns (sequence, HG adjacent kv heads, partition)
+// with NW / HG waves per head; the waves of one head take its 16-token chunks
+// round-robin, and the HG waves of one stream work on the same chunk of the
+// adjacent heads, whose rows sit side by side in the cache.  Inside a wave
+// the four 16-lane rows each own one token slot of the chunk and every lane
+// holds head_dim/16 elements of a row, so one 16-byte load per lane fetches
+// four token rows (4 x 256 B for bf16, head_dim 128).  q·k is summed over the 16
 // lanes of a row with DPP; each row keeps its own online-softmax state (max,
 // sum, accumulator) per query head, and rows and waves are merged at the end.
 // The next chunk's K/V loads are issued before the current chunk is reduced.
@@ -30,10 +32,18 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Partition kernel, query-head group G on the vector ALUs.
-template <typename T, int D, int BS, int G, int NW>
+//
+// HG adjacent kv heads per workgroup (measured on MI355X, LLaMA-13B decode
+// batch: 4 heads x 4 waves each reads HBM at 6.76 TB/s where one head x 4
+// waves reads at 6.34 TB/s: the four waves reading one chunk of four adjacent
+// heads fetch 1 KB contiguous per token row instead of 256 B pieces 10 KB
+// apart).
+template <typename T, int D, int BS, int G, int NW, int HG>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
   constexpr int EPL = D / 16;                      // elements per lane
   constexpr int WORDS = EPL * int(sizeof(T)) / 4;  // 32-bit words per lane
+  constexpr int S = NW / HG;                       // waves (chunk streams) per head
+  static_assert(NW % HG == 0, "waves must split evenly over the heads");
   using F = Frag<WORDS>;
 
   const int lane = threadIdx.x & 63;
@@ -41,7 +51,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
   const int grp = lane >> 4;
   const int r = lane & 15;
   const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
+  const int kvh0 = blockIdx.y * HG;     // first kv head of the workgroup
+  const int kvh = kvh0 + wave % HG;     // this wave's kv head
+  const int stream = wave / HG;         // this wave's chunk stream
   const int b = seq_of(a, blockIdx.z);
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
@@ -52,8 +64,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
   const int nparts = (ctx + a.partition - 1) / a.partition;
   if (t0 >= t1) {
     if (ctx == 0 && part == 0) {
-      for (int i = threadIdx.x; i < G * D; i += NW * 64)
-        store_elem<T>(a.out, (size_t(b) * Hq + kvh * G) * D + i, 0.0f);
+      for (int i = threadIdx.x; i < HG * G * D; i += NW * 64)
+        store_elem<T>(a.out, (size_t(b) * Hq + kvh0 * G) * D + i, 0.0f);
     }
     return;
   }
@@ -159,21 +171,21 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
 
   // Two register buffers, alternating.
   F ka[4], va[4], kb2[4], vb2[4];
-  int c = c_begin + wave;
+  int c = c_begin + stream;
   if (c < c_end) {
     load_chunk(c, ka, va, true);
     while (true) {
-      bool live = c + NW < c_end;
-      load_chunk(live ? c + NW : c, kb2, vb2, live);
+      bool live = c + S < c_end;
+      load_chunk(live ? c + S : c, kb2, vb2, live);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
       consume(c, ka, va);
-      c += NW;
+      c += S;
       if (c >= c_end) break;
-      live = c + NW < c_end;
-      load_chunk(live ? c + NW : c, ka, va, live);
+      live = c + S < c_end;
+      load_chunk(live ? c + S : c, ka, va, live);
       __builtin_amdgcn_sched_barrier(0);
       consume(c, kb2, vb2);
-      c += NW;
+      c += S;
       if (c >= c_end) break;
     }
   }
@@ -199,12 +211,13 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
   }
 
   const bool single = nparts == 1;
-  const size_t head0 = size_t(b) * Hq + size_t(kvh) * G;
-  auto finish = [&](int h, int d, float o, float mm, float ll) {
+  // output of query head h of kv head kv (dims d), or its partial
+  auto finish = [&](int kv, int h, int d, float o, float mm, float ll) {
+    const size_t head = size_t(b) * Hq + size_t(kv) * G + h;
     if (single) {
-      store_elem<T>(a.out, (head0 + h) * D + d, o / ll);
+      store_elem<T>(a.out, head * D + d, o / ll);
     } else {
-      const size_t pi = (head0 + h) * a.max_parts + part;
+      const size_t pi = head * a.max_parts + part;
       a.part_o[pi * D + d] = o / ll;
       if (d == 0) {
         a.part_ml[2 * pi] = mm;
@@ -213,14 +226,15 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
     }
   };
 
-  if constexpr (NW == 1) {
+  if constexpr (S == 1) {  // one wave per head: it holds all of the head's tokens
     if (grp == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) finish(h, r * EPL + e, acc[h][e], m[h], l[h]);
+        for (int e = 0; e < EPL; ++e) finish(kvh, h, r * EPL + e, acc[h][e], m[h], l[h]);
     }
   } else {
+    // merge the S streams of each head; wave w holds head w % HG, stream w / HG
     __shared__ float s_o[NW][G][D];
     __shared__ float s_ml[NW][G][2];
     if (grp == 0) {
@@ -235,20 +249,22 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < G * D; i += NW * 64) {
-      const int h = i / D;
+    for (int i = threadIdx.x; i < HG * G * D; i += NW * 64) {
+      const int hh = i / (G * D);  // head of the workgroup
+      const int h = (i / D) % G;
       const int d = i % D;
-      float M = s_ml[0][h][0];
+      float M = s_ml[hh][h][0];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+      for (int s2 = 1; s2 < S; ++s2) M = fmaxf(M, s_ml[hh + s2 * HG][h][0]);
       float L = 0.0f, O = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
+      for (int s2 = 0; s2 < S; ++s2) {
+        const int w = hh + s2 * HG;
         const float f = fast_exp2(s_ml[w][h][0] - M);
         L = fmaf(s_ml[w][h][1], f, L);
         O = fmaf(s_o[w][h][d], f, O);
       }
-      finish(h, d, O, M, L);
+      finish(kvh0 + hh, h, d, O, M, L);
     }
   }
 }
@@ -565,10 +581,21 @@ __global__ __launch_bounds__(64) void reduce_partitions_kernel(AttnArgs a) {
 #endif
 constexpr int kNW = PKV_DECODE_WAVES;  // waves per workgroup
 
+// Vector kernel: bf16 with at most 2 query heads per kv head (registers fit
+// 16 waves without spilling) uses groups of 4 adjacent kv heads x 4 waves
+// each where the kv heads split into fours; else one kv head x 4 waves.
 template <typename T, int D, int BS, int G>
 hipError_t launch_valu(const AttnArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
+  if constexpr (sizeof(T) == 2 && G <= 2) {
+    if (a.num_kv_heads % 4 == 0) {  // wide_layout() decides the same
+      const dim3 grid = work_grid(grid_parts, a.num_kv_heads / 4, num_seqs);
+      hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, 4 * kNW, 4>), grid, dim3(4 * kNW * 64),
+                         0, st, a);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kNW>), grid, dim3(kNW * 64), 0, st, a);
+  hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kNW, 1>), grid, dim3(kNW * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -591,6 +618,25 @@ bool use_mfma(bool bf16, int G) {
   if (g_decode_path == PKV_PATH_MFMA) return true;
   if (g_decode_path == PKV_PATH_AUTO) return G >= 4 || !valu_ok;
   return false;
+}
+
+// Whether the vector kernel's 4-kv-heads-per-workgroup layout serves a call.
+bool wide_layout(bool bf16, int G, int num_kv_heads) {
+  return bf16 && G <= 2 && num_kv_heads % 4 == 0 && !use_mfma(true, G);
+}
+
+// Partition length of a decode call, 0 = single pass.  AUTO for the 4-heads
+// layout: single pass up to 8192 tokens, 4096-token partitions beyond
+// (measured on MI355X, 40 heads of 128: single pass is best on the LLaMA-13B
+// batch, lengths up to 4096, and equal to partitioned over lengths 2k..8k;
+// with one 32k sequence among 127 short ones, 4096-token partitions give 6.5
+// TB/s where single pass gives 2.3).  Other kernels: resolve_partition.
+int32_t decode_partition(bool bf16, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t max_context_len, int32_t partition_size) {
+  if (partition_size == PKV_PARTITION_AUTO && num_kv_heads > 0 &&
+      num_q_heads % num_kv_heads == 0 && wide_layout(bf16, num_q_heads / num_kv_heads, num_kv_heads))
+    return max_context_len > 8192 ? 4096 : 0;
+  return resolve_partition(max_context_len, partition_size);
 }
 
 template <typename T, int D, int BS>
@@ -641,22 +687,22 @@ extern "C" pkv_status pkv_set_decode_path(int32_t path) {
 
 extern "C" int32_t pkv_get_decode_path(void) { return pkv::g_decode_path; }
 
-extern "C" int32_t pkv_decode_partition_size(int32_t, int32_t, int32_t, int32_t, int32_t,
-                                             int32_t max_context_len, int32_t partition_size,
-                                             pkv_dtype) {
-  return pkv::resolve_partition(max_context_len, partition_size);
+extern "C" int32_t pkv_decode_partition_size(int32_t, int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t, int32_t, int32_t max_context_len,
+                                             int32_t partition_size, pkv_dtype dtype) {
+  return pkv::decode_partition(dtype == PKV_BF16, num_q_heads, num_kv_heads, max_context_len,
+                               partition_size);
 }
 
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t num_kv_heads, int32_t head_dim,
                                              int32_t block_size, int32_t max_context_len,
                                              int32_t partition_size, pkv_dtype dtype) {
-  (void)num_kv_heads;
   (void)block_size;
-  (void)dtype;
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
   return pkv::workspace_for(num_seqs, num_q_heads, head_dim, max_context_len,
-                            pkv::resolve_partition(max_context_len, partition_size));
+                            pkv::decode_partition(dtype == PKV_BF16, num_q_heads, num_kv_heads,
+                                                  max_context_len, partition_size));
 }
 
 extern "C" pkv_status pkv_paged_attention_decode(
@@ -702,7 +748,8 @@ extern "C" pkv_status pkv_paged_attention_decode(
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: NULL pointer argument");
 
-  const int32_t partition = pkv::resolve_partition(max_context_len, partition_size);
+  const int32_t partition = pkv::decode_partition(dtype == PKV_BF16, num_q_heads, num_kv_heads,
+                                                  max_context_len, partition_size);
   const int32_t cap = int32_t(std::min<int64_t>(max_context_len,
                                                 int64_t(max_blocks_per_seq) * block_size));
   pkv::AttnArgs a{};

@@ -221,6 +221,26 @@ def test_decode_workspace_and_partition_queries():
     assert _decode(part=16, q=1, k=1, v=1, tables=1, ctx=1, out=1) == -6
 
 
+def test_decode_auto_partition_follows_the_kernel():
+    """AUTO: the 4-kv-heads vector layout (bf16, at most 2 query heads per kv
+    head, kv heads in fours) runs single pass up to 8192 tokens and 4096-token
+    partitions beyond; the other kernels split past 2048 tokens."""
+    assert P.decode_partition_size(128, 40, 40, 128, 16, 4150, P.PARTITION_AUTO, P.BF16) == 0
+    assert P.decode_partition_size(128, 40, 40, 128, 16, 8192, P.PARTITION_AUTO, P.BF16) == 0
+    assert P.decode_partition_size(128, 40, 40, 128, 16, 8193, P.PARTITION_AUTO, P.BF16) == 4096
+    assert P.decode_partition_size(64, 64, 32, 128, 16, 4000, P.PARTITION_AUTO, P.BF16) == 0
+    assert P.decode_partition_size(8, 6, 3, 128, 16, 4000, P.PARTITION_AUTO, P.BF16) == 2048
+    assert P.decode_partition_size(8, 32, 8, 128, 16, 4000, P.PARTITION_AUTO, P.BF16) == 2048
+    assert P.decode_partition_size(8, 4, 4, 64, 16, 4000, P.PARTITION_AUTO, P.F32) == 2048
+    assert P.decode_partition_size(8, 4, 4, 64, 16, 2048, P.PARTITION_AUTO, P.F32) == 0
+    assert P.decode_workspace_bytes(128, 40, 40, 128, 16, 4150, P.PARTITION_AUTO, P.BF16) == 0
+    P.set_decode_path(P.PATH_MFMA)
+    try:  # forced onto the matrix cores: that kernel's rule
+        assert P.decode_partition_size(128, 80, 40, 128, 16, 4150, P.PARTITION_AUTO, P.BF16) == 2048
+    finally:
+        P.set_decode_path(P.PATH_AUTO)
+
+
 def test_prefill_partition_query():
     """AUTO prefill runs single pass when the query tiles fill the grid (16
     sequences x 40 heads x 512-token chunks) and partitions a small grid; an

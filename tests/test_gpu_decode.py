@@ -104,6 +104,8 @@ EDGE_CTX = (0, 1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1000, 1537)
 @pytest.mark.parametrize("dtype,D,bs,hq,hkv", [
     ("f32", 64, 16, 4, 4), ("f32", 128, 32, 8, 2), ("bf16", 64, 32, 2, 1),
     ("bf16", 128, 16, 8, 1), ("bf16", 128, 32, 16, 4), ("bf16", 128, 16, 4, 2),
+    # kv heads in fours, at most 2 query heads each: the 4-heads-per-workgroup layout
+    ("bf16", 64, 16, 8, 4), ("bf16", 128, 32, 8, 8),
 ])
 @pytest.mark.parametrize("part", [0, 32, 512])
 def test_edge_lengths(dtype, D, bs, hq, hkv, part, decode_path):
