@@ -307,18 +307,22 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
 constexpr bool kMfmaKNT = PKV_MFMA_K_NT;
 constexpr bool kMfmaVNT = PKV_MFMA_V_NT;
 
-template <int D, int BS, int NW>
+template <int D, int BS, int NW, int HG>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 32;  // q.K^T MFMA steps over head_dim
   constexpr int EPL = D / 16;     // V elements per lane per token row = PV tiles
   constexpr int VW = EPL / 2;     // 32-bit words per V load
+  constexpr int S = NW / HG;      // waves (chunk streams) per kv head
+  static_assert(NW % HG == 0, "waves must split evenly over the heads");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane >> 4;
   const int n = lane & 15;
   const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
+  const int kvh0 = blockIdx.y * HG;  // first kv head of the workgroup
+  const int kvh = kvh0 + wave % HG;  // this wave's kv head
+  const int stream = wave / HG;      // this wave's chunk stream
   const int b = seq_of(a, blockIdx.z);
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
@@ -332,13 +336,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
   const int nparts = (ctx + a.partition - 1) / a.partition;
   const int rows = G;  // valid operand columns
   const bool row_ok = n < rows;
-  auto out_row = [&](int r) {  // (sequence, query head) index of column r
-    return size_t(b) * Hq + size_t(kvh) * G + r;
+  auto out_row_of = [&](int kv, int r) {  // (sequence, query head) index of column r
+    return size_t(b) * Hq + size_t(kv) * G + r;
   };
+  auto out_row = [&](int r) { return out_row_of(kvh, r); };
   if (t0 >= t1) {
-    if (ctx == 0 && part == 0)  // nothing visible: zero outputs
-      for (int i = threadIdx.x; i < rows * D; i += NW * 64)
-        store_elem<uint16_t>(a.out, out_row(i / D) * D + i % D, 0.0f);
+    if (ctx == 0 && part == 0)  // nothing visible: zero outputs (HG heads, contiguous)
+      for (int i = threadIdx.x; i < HG * rows * D; i += NW * 64)
+        store_elem<uint16_t>(a.out, out_row_of(kvh0, 0) * D + i, 0.0f);
     return;
   }
 
@@ -461,9 +466,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
     }
   };
 
-  constexpr int WSTEP = NW;  // chunks between one wave's iterations
+  constexpr int WSTEP = S;  // chunks between one wave's iterations
   Regs ra, rb;
-  int ch = c_begin + wave;
+  int ch = c_begin + stream;
   if (ch < c_end) {
     load_chunk(ch, ra, true);
     while (true) {
@@ -488,12 +493,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
   // acc[t][r] = O[row n][EPL*(4c + r) + t] (unnormalised, this wave's tokens).
   // A row with no visible token in this partition has l = 0 and stores zeros.
   const bool single = nparts == 1;
-  auto finish = [&](int row, int d, float o, float mm, float ll) {
+  auto finish = [&](int kv, int row, int d, float o, float mm, float ll) {
     const float v = ll > 0.0f ? o / ll : 0.0f;
     if (single) {
-      store_elem<uint16_t>(a.out, out_row(row) * D + d, v);
+      store_elem<uint16_t>(a.out, out_row_of(kv, row) * D + d, v);
     } else {
-      const size_t pi = out_row(row) * a.max_parts + part;
+      const size_t pi = out_row_of(kv, row) * a.max_parts + part;
       a.part_o[pi * D + d] = v;
       if (d == 0) {
         a.part_ml[2 * pi] = mm;
@@ -501,14 +506,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
       }
     }
   };
-  if constexpr (NW == 1) {  // this wave holds all of its rows' tokens
+  if constexpr (S == 1) {  // this wave holds all of its rows' tokens
     if (row_ok) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int t = 0; t < EPL; ++t) finish(n, EPL * (4 * c + r) + t, acc[t][r], m, l);
+        for (int t = 0; t < EPL; ++t) finish(kvh, n, EPL * (4 * c + r) + t, acc[t][r], m, l);
     }
   } else {
+    // merge the S streams of each head; wave w holds head w % HG, stream w / HG
     __shared__ float s_o[NW][16][D];
     __shared__ float s_ml[NW][16][2];
 #pragma unroll
@@ -520,20 +526,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
       s_ml[wave][n][1] = l;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < rows * D; i += NW * 64) {
-      const int h = i / D;
+    for (int i = threadIdx.x; i < HG * rows * D; i += NW * 64) {
+      const int hh = i / (rows * D);  // head of the workgroup
+      const int h = (i / D) % rows;
       const int d = i % D;
-      float M = s_ml[0][h][0];
+      float M = s_ml[hh][h][0];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+      for (int s2 = 1; s2 < S; ++s2) M = fmaxf(M, s_ml[hh + s2 * HG][h][0]);
       float L = 0.0f, O = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
+      for (int s2 = 0; s2 < S; ++s2) {
+        const int w = hh + s2 * HG;
         const float f = fast_exp2(s_ml[w][h][0] - M);
         L = fmaf(s_ml[w][h][1], f, L);
         O = fmaf(s_o[w][h][d], f, O);
       }
-      finish(h, d, O, M, L);
+      finish(kvh0 + hh, h, d, O, M, L);
     }
   }
 }
@@ -584,13 +592,22 @@ constexpr int kNW = PKV_DECODE_WAVES;  // waves per workgroup
 // Vector kernel: bf16 with at most 2 query heads per kv head (registers fit
 // 16 waves without spilling) uses groups of 4 adjacent kv heads x 4 waves
 // each where the kv heads split into fours; else one kv head x 4 waves.
+#ifndef PKV_VALU_HG
+#define PKV_VALU_HG 4
+#endif
+#ifndef PKV_VALU_WAVES
+#define PKV_VALU_WAVES 16
+#endif
+constexpr int kValuHG = PKV_VALU_HG;     // adjacent kv heads per workgroup (wide layout)
+constexpr int kValuNW = PKV_VALU_WAVES;  // waves per workgroup (wide layout)
+
 template <typename T, int D, int BS, int G>
 hipError_t launch_valu(const AttnArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
   if constexpr (sizeof(T) == 2 && G <= 2) {
     if (a.num_kv_heads % 4 == 0) {  // wide_layout() decides the same
-      const dim3 grid = work_grid(grid_parts, a.num_kv_heads / 4, num_seqs);
-      hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, 4 * kNW, 4>), grid, dim3(4 * kNW * 64),
-                         0, st, a);
+      const dim3 grid = work_grid(grid_parts, a.num_kv_heads / kValuHG, num_seqs);
+      hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kValuNW, kValuHG>), grid,
+                         dim3(kValuNW * 64), 0, st, a);
       return hipGetLastError();
     }
   }
@@ -599,10 +616,25 @@ hipError_t launch_valu(const AttnArgs& a, int num_seqs, hipStream_t st, int grid
   return hipGetLastError();
 }
 
+#ifndef PKV_MFMA_HG
+#define PKV_MFMA_HG 1
+#endif
+#ifndef PKV_MFMA_WAVES
+#define PKV_MFMA_WAVES 4
+#endif
+constexpr int kMfmaHG = PKV_MFMA_HG;     // adjacent kv heads per workgroup
+constexpr int kMfmaNW = PKV_MFMA_WAVES;  // waves per workgroup
+
 template <int D, int BS>
 hipError_t launch_mfma(const AttnArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
-  const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW>), grid, dim3(kNW * 64), 0, st, a);
+  if (kMfmaHG > 1 && a.num_kv_heads % kMfmaHG == 0) {
+    const dim3 grid = work_grid(grid_parts, a.num_kv_heads / kMfmaHG, num_seqs);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kMfmaNW, kMfmaHG>), grid, dim3(kMfmaNW * 64), 0,
+                       st, a);
+  } else {
+    const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW, 1>), grid, dim3(kNW * 64), 0, st, a);
+  }
   return hipGetLastError();
 }
 
