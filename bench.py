@@ -630,7 +630,8 @@ def main() -> int:
             "decode_path": args.path, "launch_order": args.order, "chunk_tokens": chunk,
         },
         "roofline": {
-            "kernel": "paged_attention_decode (partition kernel + log-sum-exp merge)",
+            "kernel": ("paged_attention_decode (single pass)" if part_used == 0 else
+                       "paged_attention_decode (partition kernel + log-sum-exp merge)"),
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "avg_launch_us": round(dec_avg_s * 1e6, 2),
