@@ -18,17 +18,19 @@ namespace {
 // ---------------------------------------------------------------------------
 // Chunked prefill on the matrix cores, K/V shared through LDS.
 //
-// A workgroup of NWP waves owns NWP query tiles of one (sequence, kv head,
-// partition); a tile is 16 (query, head) rows, floor(16 / G) consecutive
-// queries times the G query heads of the kv head, the 16 operand columns of
-// the matrix products (the decode kernel's layout, with queries added).  Each
-// 16-token K/V chunk is loaded once by the whole workgroup — whole rows,
-// streamed — into a double-buffered LDS tile, and every wave runs its
-// q.K^T and P.V products on it, so K/V cross the caches once per workgroup
-// instead of once per tile.  The next chunk's loads are in flight while the
-// current one is computed.  Waves whose tile sees no token of a chunk (the
-// causal boundary) skip its math but keep to the barriers.
-template <int D, int BS, int NWP>
+// A workgroup of NWP waves owns NWP * TPW query tiles of one (sequence, kv
+// head, partition); a tile is 16 (query, head) rows, floor(16 / G)
+// consecutive queries times the G query heads of the kv head, the 16 operand
+// columns of the matrix products (the decode kernel's layout, with queries
+// added), and each wave owns TPW consecutive tiles.  Each 16-token K/V chunk
+// is loaded once by the whole workgroup — whole rows, streamed — into a
+// double-buffered LDS tile; every wave reads each K and V operand from LDS
+// once and uses it for all of its tiles (LDS reads per flop fall with TPW),
+// and packs the V operand once for all of them.  The next chunk's loads are
+// in flight while the current one is computed.  Tiles that see no token of a
+// chunk (the causal boundary) skip its math; their waves keep to the
+// barriers.
+template <int D, int BS, int NWP, int TPW>
 __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 32;
   constexpr int EPL = D / 16;
@@ -37,7 +39,6 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   constexpr int PITCH = RB + 16;       // padded LDS row pitch
   constexpr int LPR = RB / 16;         // 16-byte pieces per row
   constexpr int PIECES = 16 * LPR;     // pieces per 16-token chunk, per cache
-  static_assert(2 * PIECES <= NWP * 64 * 2, "chunk loads cover at most two pieces per lane");
   __shared__ __attribute__((aligned(16))) char s_kv[2][2][16 * PITCH];  // [buffer][K/V]
 
   const int lane = threadIdx.x & 63;
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   const int n = lane & 15;
   const int part = blockIdx.x;
   const int kvh = int(blockIdx.y) % a.num_kv_heads;
-  const int tile = (int(blockIdx.y) / a.num_kv_heads) * NWP + wave;
+  const int tile0 = ((int(blockIdx.y) / a.num_kv_heads) * NWP + wave) * TPW;  // first own tile
   const int b = seq_of(a, blockIdx.z);
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
@@ -57,47 +58,64 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   int qrow0, nq;
   query_range(a, b, qrow0, nq);
   // workgroup-wide token range: the causal end of its last tile with queries
-  const int g_first = (int(blockIdx.y) / a.num_kv_heads) * NWP * QPT;
+  const int g_first = (int(blockIdx.y) / a.num_kv_heads) * NWP * TPW * QPT;
   if (g_first >= nq) return;  // uniform over the workgroup
-  const int g_last = min(g_first + NWP * QPT, nq) - 1;
+  const int g_last = min(g_first + NWP * TPW * QPT, nq) - 1;
   const int t0 = part * a.partition;
   const int g_end = max(0, ctx - nq + g_last + 1);
   const int g_t1 = min(g_end, t0 + a.partition);
 
-  // this wave's tile
-  const int q_first = tile * QPT;
-  const bool has_tile = q_first < nq;
-  const int q_last = has_tile ? min(q_first + QPT, nq) - 1 : q_first;
-  const int t_end = has_tile ? max(0, ctx - nq + q_last + 1) : 0;
-  const int t1 = min(t_end, t0 + a.partition);
-  const int nparts = (t_end + a.partition - 1) / a.partition;
-  const int rows = has_tile ? (q_last - q_first + 1) * G : 0;
-  const bool row_ok = n < rows;
-  const int qi = q_first + (row_ok ? n / G : 0);
-  const int pos_n = row_ok ? ctx - nq + qi : -1;
-  auto out_row = [&](int r) {
-    return (size_t(qrow0) + q_first + r / G) * Hq + size_t(kvh) * G + r % G;
+  // this wave's tiles (all fields wave-uniform except the per-lane row ones)
+  int q_first[TPW], t_end[TPW], t1[TPW], rows[TPW], pos_n[TPW], pos_lo[TPW];
+  bool has_tile[TPW], row_ok[TPW];
+  int t1_max = 0;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    q_first[u] = (tile0 + u) * QPT;
+    has_tile[u] = q_first[u] < nq;
+    const int q_last = has_tile[u] ? min(q_first[u] + QPT, nq) - 1 : q_first[u];
+    t_end[u] = has_tile[u] ? max(0, ctx - nq + q_last + 1) : 0;
+    t1[u] = min(t_end[u], t0 + a.partition);
+    t1_max = max(t1_max, t1[u]);
+    rows[u] = has_tile[u] ? (q_last - q_first[u] + 1) * G : 0;
+    row_ok[u] = n < rows[u];
+    const int qi = q_first[u] + (row_ok[u] ? n / G : 0);
+    pos_n[u] = row_ok[u] ? ctx - nq + qi : -1;
+    pos_lo[u] = ctx - nq + q_first[u];  // position of the tile's first query
+  }
+  auto out_row = [&](int u, int r) {
+    return (size_t(qrow0) + q_first[u] + r / G) * Hq + size_t(kvh) * G + r % G;
+  };
+  auto zero_tile = [&](int u) {
+    for (int i = lane; i < rows[u] * D; i += 64)
+      store_elem<uint16_t>(a.out, out_row(u, i / D) * D + i % D, 0.0f);
   };
   if (t0 >= g_t1) {  // uniform: no token of this partition for any tile
-    if (part == 0 && has_tile && t_end == 0)
-      for (int i = lane; i < rows * D; i += 64)
-        store_elem<uint16_t>(a.out, out_row(i / D) * D + i % D, 0.0f);
+    if (part == 0)
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        if (has_tile[u] && t_end[u] == 0) zero_tile(u);
     return;
   }
 
-  uint4 qop[KSTEPS];
-  {
-    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + out_row(row_ok ? n : 0) * D + 8 * c;
+  uint4 qop[TPW][KSTEPS];
+  f32x4_t acc[TPW][EPL];
+  float m[TPW], l[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const uint16_t* qh =
+        static_cast<const uint16_t*>(a.q) + out_row(u, row_ok[u] ? n : 0) * D + 8 * c;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qh + 32 * j);
-      qop[j] = row_ok ? v : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v = row_ok[u] ? *reinterpret_cast<const uint4*>(qh + 32 * j)
+                                : make_uint4(0u, 0u, 0u, 0u);
+      qop[u][j] = v;
     }
-  }
-  f32x4_t acc[EPL];
 #pragma unroll
-  for (int t = 0; t < EPL; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -FLT_MAX, l = 0.0f;
+    for (int t = 0; t < EPL; ++t) acc[u][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m[u] = -FLT_MAX;
+    l[u] = 0.0f;
+  }
 
   const int row_stride = Hkv * D;
   const char* kc = static_cast<const char*>(a.k_cache);
@@ -141,17 +159,23 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
 
   auto compute = [&](int ch, int buf) {
     const int tc = ch * kChunk;
-    if (tc >= t1) return;  // this tile sees no token of this chunk
+    if (tc >= t1_max) return;  // none of this wave's tiles sees a token of this chunk
     const char* ks = s_kv[buf][0];
     const char* vs = s_kv[buf][1];
-    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+    // S^T = K . Q^T for every tile, each K operand read once
+    f32x4_t s[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) s[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
-      const uint4 kop = *reinterpret_cast<const uint4*>(ks + n * PITCH + 16 * c + 64 * j);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
-                                                  __builtin_bit_cast(bf16x8_t, qop[j]), s, 0, 0,
-                                                  0);
+      const bf16x8_t kop =
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ks + n * PITCH + 16 * c + 64 * j));
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, __builtin_bit_cast(bf16x8_t, qop[u][j]),
+                                                       s[u], 0, 0, 0);
     }
+    // V^T operands: element t of rows 4c..4c+3 (dims EPL*n ..), packed once
     uint32_t v[4][VW];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -168,29 +192,7 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
         v[i][1] = x.y;
       }
     }
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = tc + 4 * c + i;
-      sc[i] = (t < t1 && t <= pos_n) ? s[i] * a.scale_log2 : -INFINITY;
-    }
-    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    if (__ballot(mx > m + kLazyMax)) {
-      float hm = fmaxf(mx, __shfl_xor(mx, 16));
-      hm = fmaxf(hm, __shfl_xor(hm, 32));
-      const float mn = hm > m + kLazyMax ? hm : m;
-      const float alpha = fast_exp2(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
-      m = mn;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    const s16x4_t pb =
-        __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+    s16x4_t vb[EPL];
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
       const int w = t >> 1;
@@ -202,8 +204,42 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
         lo = (v[0][w] & 0xFFFFu) | (v[1][w] << 16);
         hi = (v[2][w] & 0xFFFFu) | (v[3][w] << 16);
       }
-      const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pb, acc[t], 0, 0, 0);
+      vb[t] = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (tc >= t1[u]) continue;  // wave-uniform
+      float sc[4];
+      if (tc + kChunk <= t1[u] && tc + kChunk - 1 <= pos_lo[u]) {  // every row sees every token
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = s[u][i] * a.scale_log2;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tc + 4 * c + i;
+          sc[i] = (t < t1[u] && t <= pos_n[u]) ? s[u][i] * a.scale_log2 : -INFINITY;
+        }
+      }
+      const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (__ballot(mx > m[u] + kLazyMax)) {
+        float hm = fmaxf(mx, __shfl_xor(mx, 16));
+        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        const float mn = hm > m[u] + kLazyMax ? hm : m[u];
+        const float alpha = fast_exp2(m[u] - mn);
+        l[u] *= alpha;
+#pragma unroll
+        for (int t = 0; t < EPL; ++t) acc[u][t] *= alpha;
+        m[u] = mn;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m[u]);
+      l[u] += (p[0] + p[1]) + (p[2] + p[3]);
+      const s16x4_t pb = __builtin_bit_cast(
+          s16x4_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+#pragma unroll
+      for (int t = 0; t < EPL; ++t)
+        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb[t], pb, acc[u][t], 0, 0, 0);
     }
   };
 
@@ -221,35 +257,38 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
     buf ^= 1;
   }
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!has_tile) return;
-  if (t_end == 0) {  // every query of this tile sits before position 0
-    if (part == 0)
-      for (int i = lane; i < rows * D; i += 64)
-        store_elem<uint16_t>(a.out, out_row(i / D) * D + i % D, 0.0f);
-    return;
-  }
-  if (part >= nparts) return;
-  const bool single = nparts == 1;
-  if (row_ok) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int u = 0; u < TPW; ++u) {
+    float lu = l[u];
+    lu += __shfl_xor(lu, 16);
+    lu += __shfl_xor(lu, 32);
+    if (!has_tile[u]) continue;
+    if (t_end[u] == 0) {  // every query of this tile sits before position 0
+      if (part == 0) zero_tile(u);
+      continue;
+    }
+    const int nparts = (t_end[u] + a.partition - 1) / a.partition;
+    if (part >= nparts) continue;
+    const bool single = nparts == 1;
+    if (row_ok[u]) {
 #pragma unroll
-      for (int t = 0; t < EPL; ++t) {
-        const int d = EPL * (4 * c + r) + t;
-        const float o = l > 0.0f ? acc[t][r] / l : 0.0f;
-        if (single) {
-          store_elem<uint16_t>(a.out, out_row(n) * D + d, o);
-        } else {
-          const size_t pi = out_row(n) * a.max_parts + part;
-          a.part_o[pi * D + d] = o;
-          if (d == 0) {
-            a.part_ml[2 * pi] = m;
-            a.part_ml[2 * pi + 1] = l;
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < EPL; ++t) {
+          const int d = EPL * (4 * c + r) + t;
+          const float o = lu > 0.0f ? acc[u][t][r] / lu : 0.0f;
+          if (single) {
+            store_elem<uint16_t>(a.out, out_row(u, n) * D + d, o);
+          } else {
+            const size_t pi = out_row(u, n) * a.max_parts + part;
+            a.part_o[pi * D + d] = o;
+            if (d == 0) {
+              a.part_ml[2 * pi] = m[u];
+              a.part_ml[2 * pi + 1] = lu;
+            }
           }
         }
-      }
+    }
   }
 }
 
@@ -295,21 +334,38 @@ __global__ __launch_bounds__(256) void merge_prefill_kernel(AttnArgs a) {
 // Host side.
 
 
-// Query tiles (one wave each) per prefill workgroup: as many as the longest
-// chunk fills, up to 16, so every K/V chunk read from HBM serves up to 16
-// tiles.
-int prefill_waves(int q_tiles) { return q_tiles > 8 ? 16 : q_tiles > 4 ? 8 : 4; }
+// Measured on MI355X (16 sequences x 40 heads, 512-token chunks): 16 waves x
+// 1 tile 475 TFLOP/s, 8 x 2 409, 4 x 2 361, 4 x 4 262 — more tiles per wave
+// halve the LDS reads per flop but lengthen each wave's dependent chain
+// between the per-chunk barriers, which costs more.
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 16
+#endif
+#ifndef PKV_PREFILL_TPW
+#define PKV_PREFILL_TPW 1
+#endif
+constexpr int kPrefillNW = PKV_PREFILL_WAVES;  // waves per workgroup, long chunks
+constexpr int kPrefillTPW = PKV_PREFILL_TPW;   // query tiles per wave, long chunks
+
+// Query tiles per prefill workgroup: long chunks use kPrefillNW waves of
+// kPrefillTPW tiles each; shorter ones as many single-tile waves (4 or 8) as
+// they fill.  Every K/V chunk read from HBM serves all tiles of a workgroup.
+int prefill_tiles_per_group(int q_tiles) {
+  return q_tiles > 8 ? kPrefillNW * kPrefillTPW : q_tiles > 4 ? 8 : 4;
+}
+
 template <int D, int BS>
 hipError_t launch_prefill(const AttnArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
-  const int nw = prefill_waves(a.q_tiles);
-  const int groups = (a.q_tiles + nw - 1) / nw;
+  const int tpg = prefill_tiles_per_group(a.q_tiles);
+  const int groups = (a.q_tiles + tpg - 1) / tpg;
   const dim3 grid = work_grid(grid_parts, a.num_kv_heads * groups, num_seqs);
-  if (nw == 16)
-    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, 16>), grid, dim3(16 * 64), 0, st, a);
-  else if (nw == 8)
-    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, 8>), grid, dim3(8 * 64), 0, st, a);
+  if (a.q_tiles > 8)
+    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, kPrefillNW, kPrefillTPW>), grid,
+                       dim3(kPrefillNW * 64), 0, st, a);
+  else if (tpg == 8)
+    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, 8, 1>), grid, dim3(8 * 64), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, 4>), grid, dim3(4 * 64), 0, st, a);
+    hipLaunchKernelGGL((prefill_lds_kernel<D, BS, 4, 1>), grid, dim3(4 * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.partition >= kSingle) return e;
   hipLaunchKernelGGL((merge_prefill_kernel<D>), dim3(1, a.num_kv_heads * a.q_tiles, num_seqs),
@@ -329,8 +385,8 @@ int32_t prefill_partition(int32_t num_seqs, int32_t max_queries_per_seq, int32_t
   const int G = num_q_heads / num_kv_heads;
   const int qpt = 16 / G > 0 ? 16 / G : 1;
   const int64_t tiles = (int64_t(max_queries_per_seq) + qpt - 1) / qpt;
-  const int64_t nw = prefill_waves(int(std::min<int64_t>(tiles, 1 << 20)));
-  const int64_t groups = (tiles + nw - 1) / nw;
+  const int64_t tpg = prefill_tiles_per_group(int(std::min<int64_t>(tiles, 1 << 20)));
+  const int64_t groups = (tiles + tpg - 1) / tpg;
   return int64_t(num_seqs) * num_kv_heads * groups >= 1024
              ? 0
              : resolve_partition(max_context_len, partition_size);
