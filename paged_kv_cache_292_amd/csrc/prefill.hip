@@ -127,26 +127,33 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   // Cooperative chunk load: piece p (< 2 * PIECES) of the chunk is 16 bytes of
   // K (p < PIECES) or V, token p % PIECES / LPR, bytes 16 * (p % LPR).
   constexpr int PER_LANE = (2 * PIECES + NWP * 64 - 1) / (NWP * 64);
-  uint4 stage[PER_LANE];
-  auto fetch = [&](int ch) {
+  using Stage = uint4[PER_LANE];
+  // `live` false: the prefetch past the last chunk, issued anyway so that no
+  // branch hides the loads from the wait-count tracking; every lane then
+  // reads the cache's first 16 bytes (one line per wave).
+  auto fetch = [&](int ch, Stage& stage, bool live) {
     const int tc = __builtin_amdgcn_readfirstlane(ch * kChunk);
     int bid = scalar_read(tbl + tc / BS);
     bid = (unsigned)bid < (unsigned)a.num_blocks ? bid : 0;
-    const size_t rowbase = ((size_t(bid) * BS + (tc % BS)) * row_stride + size_t(kvh) * D) * 2;
+    const size_t rowbase =
+        live ? ((size_t(bid) * BS + (tc % BS)) * row_stride + size_t(kvh) * D) * 2 : 0;
 #pragma unroll
     for (int k = 0; k < PER_LANE; ++k) {
-      const int p = threadIdx.x + k * NWP * 64;
-      if (p < 2 * PIECES) {
-        const int pp = p % PIECES;
-        const int tok = pp / LPR;
-        const char* base = (p < PIECES ? kc : vc) + rowbase;
-        // rows past the range re-read the chunk's first row (masked later)
-        const uint32_t off = uint32_t((tc + tok < g_t1 ? tok * row_stride * 2 : 0) + 16 * (pp % LPR));
-        stage[k] = load16<true>(base + off);
-      }
+      // every lane loads (lanes past the chunk's pieces re-read piece 0 and
+      // store nothing), so no lane-masked branch hides the loads from the
+      // compiler's wait-count tracking
+      const int p0 = threadIdx.x + k * NWP * 64;
+      const int p = p0 < 2 * PIECES ? p0 : 0;
+      const int pp = p % PIECES;
+      const int tok = pp / LPR;
+      const char* base = (p < PIECES ? kc : vc) + rowbase;
+      // rows past the range re-read the chunk's first row (masked later)
+      const uint32_t off =
+          !live ? 0u : uint32_t((tc + tok < g_t1 ? tok * row_stride * 2 : 0) + 16 * (pp % LPR));
+      stage[k] = load16<true>(base + off);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const Stage& stage) {
 #pragma unroll
     for (int k = 0; k < PER_LANE; ++k) {
       const int p = threadIdx.x + k * NWP * 64;
@@ -243,18 +250,35 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
     }
   };
 
-  // pipeline: fetch(next) overlaps compute(current); one barrier per chunk
-  fetch(c_begin);
-  store(0);
-  __syncthreads();
-  int buf = 0;
-  for (int ch = c_begin; ch < c_end; ++ch) {
-    const bool more = ch + 1 < c_end;
-    if (more) fetch(ch + 1);
-    compute(ch, buf);
-    if (more) store(buf ^ 1);
+  // Pipeline, prefetch distance 4: the global loads of chunk x + 4 are
+  // issued before chunk x is computed and reach LDS only after chunk x + 3 is
+  // computed, so four chunks are in flight per workgroup.  With one chunk in
+  // flight the loads, not the math, set the pace (measured: 2.3x slower than
+  // the same kernel without global loads): a workgroup needs tens of KB in
+  // flight to cover the memory latency.  Four register stages rotate; two LDS
+  // buffers alternate by the chunk's parity; one barrier per chunk.  The loop
+  // starts four chunks early (those steps only fetch and store), so every
+  // fetch comes from the same loop body.
+  // the query operands (loaded above) are complete before the pipeline
+  // starts, so no wait inside it has to cover them
+  __builtin_amdgcn_s_waitcnt(0);
+  constexpr int NST = 4;
+  Stage st0, st1, st2, st3;
+  // step of chunk x (its register stage `mine`, the next chunk's `next`)
+  auto step = [&](int x, Stage& mine, const Stage& next, int buf) {
+    fetch(x + NST < c_end ? x + NST : c_begin, mine, x + NST < c_end);
+    if (x >= c_begin) compute(x, buf);
+    if (x + 1 >= c_begin && x + 1 < c_end) store(buf ^ 1, next);
     __syncthreads();
-    buf ^= 1;
+  };
+  for (int x = c_begin - NST; x < c_end; x += NST) {
+    step(x, st0, st1, 0);
+    if (x + 1 >= c_end) break;
+    step(x + 1, st1, st2, 1);
+    if (x + 2 >= c_end) break;
+    step(x + 2, st2, st3, 0);
+    if (x + 3 >= c_end) break;
+    step(x + 3, st3, st0, 1);
   }
 
 #pragma unroll
