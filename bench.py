@@ -44,6 +44,9 @@ def _args():
                     help="decode kernel: automatic choice, vector ALUs or matrix cores")
     ap.add_argument("--order", choices=["longest", "index"], default="longest",
                     help="launch order of the sequences handed to the decode kernel")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write the step's new tokens with its own cache-write launch instead "
+                         "of the decode call that writes them (paged_attention_decode_write)")
     ap.add_argument("--serial-upload", action="store_true",
                     help="upload each step's tables on the compute stream instead of a side "
                          "stream overlapped with the previous step's attention")
@@ -533,6 +536,8 @@ def main() -> int:
     E = s.elem_bytes
 
     qrows = chunk if chunk else 1  # query rows per sequence
+    # decode steps with new tokens write them inside the decode launch
+    fused_write = bool(step_new) and not chunk and not args.separate_write
 
     def decode_bytes(ctx):
         """Unique K/V bytes of the step's sequences, and those plus q, out,
@@ -540,6 +545,8 @@ def main() -> int:
         kv = int(ctx.sum()) * 2 * Hkv * D * E
         nb = int(((ctx + bs - 1) // bs).sum())
         other = 2 * B * qrows * Hq * D * E + 4 * nb + 4 * B
+        if fused_write:  # the new rows read from the input and written into the cache
+            other += 2 * 2 * B * Hkv * D * E
         if part_used > 0:
             np_ = (ctx + part_used - 1) // part_used
             multi = np_[np_ > 1].sum()
@@ -592,7 +599,7 @@ def main() -> int:
         copied[j].record(up_stream)
         up_done[ds].record(up_stream)
         stream.wait_event(up_done[ds])
-        if step_tok:
+        if step_tok and not fused_write:
             P.kv_reshape_and_cache(new_k_steps[i], new_v_steps[i], k_cache, v_cache, d_slots)
         if i in ev:
             ev[i][0].record(stream)
@@ -600,6 +607,11 @@ def main() -> int:
             P.paged_attention_prefill(out, q, d_qstart, chunk, k_cache, v_cache, d_tables, d_ctx,
                                       maxc, s.scale, args.partition, workspace,
                                       seq_order=d_order if use_order else None)
+        elif fused_write:
+            P.paged_attention_decode_write(out, q, new_k_steps[i], new_v_steps[i], k_cache,
+                                           v_cache, d_tables, d_ctx, maxc, s.scale,
+                                           args.partition, workspace,
+                                           seq_order=d_order if use_order else None)
         else:
             P.paged_attention_decode(out, q, k_cache, v_cache, d_tables, d_ctx, maxc, s.scale,
                                      args.partition, workspace,
@@ -658,8 +670,9 @@ def main() -> int:
             "decode_path": args.path, "launch_order": args.order, "chunk_tokens": chunk,
         },
         "roofline": {
-            "kernel": ("paged_attention_decode (single pass)" if part_used == 0 else
-                       "paged_attention_decode (partition kernel + log-sum-exp merge)"),
+            "kernel": ("paged_attention_decode" + ("_write (cache write fused)" if fused_write else "")
+                       + (" (single pass)" if part_used == 0 else
+                          " (partition kernel + log-sum-exp merge)")),
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "avg_launch_us": round(dec_avg_s * 1e6, 2),

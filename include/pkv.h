@@ -180,6 +180,36 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q,
                                       size_t workspace_bytes, pkv_dtype dtype,
                                       void* stream);
 
+/* The decode step in one launch (the cache write fused into the attention):
+ * for every sequence b with context_lens[b] > 0, its new token is its last
+ * position p = context_lens[b] - 1 (already appended by the allocator), and
+ * new_key[b] / new_value[b] (device, num_kv_heads x head_dim elements from
+ * element b * key_seq_stride / b * value_seq_stride) are written into the
+ * caches at the slot the block table gives for p; then the result is that
+ * of pkv_paged_attention_decode.  Equivalent to pkv_kv_reshape_and_cache of
+ * those rows at those slots followed by pkv_paged_attention_decode, in one
+ * kernel (plus the merge when partitioned): the row of p is read from
+ * new_key / new_value, never from the slot being written.  Strides must be
+ * >= num_kv_heads * head_dim and multiples of 16 bytes; pointers 16-byte
+ * aligned (PKV_ERR_INVALID_ARG otherwise).  A table entry outside the pool
+ * skips the write.  Other arguments and errors as pkv_paged_attention_decode.
+ */
+pkv_status pkv_paged_attention_decode_write(void* out, const void* q,
+                                            const void* new_key, const void* new_value,
+                                            int64_t key_seq_stride, int64_t value_seq_stride,
+                                            void* k_cache, void* v_cache,
+                                            const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens,
+                                            const int32_t* seq_order,
+                                            int32_t max_context_len, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t block_size,
+                                            int32_t num_blocks, float scale,
+                                            int32_t partition_size, void* workspace,
+                                            size_t workspace_bytes, pkv_dtype dtype,
+                                            void* stream);
+
 /* ------------------------------------------------------------------------
  * Chunked prefill: several new tokens per sequence attend to the paged cache
  * (long prompts are processed in pieces so that one large prefill does not

@@ -17,7 +17,8 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "lib", "PkvError", "F32", "BF16", "PARTITION_AUTO",
-    "kv_reshape_and_cache", "paged_attention_decode", "decode_workspace_bytes",
+    "kv_reshape_and_cache", "paged_attention_decode", "paged_attention_decode_write",
+    "decode_workspace_bytes",
     "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned", "longest_first_order",
     "paged_attention_prefill", "prefill_workspace_bytes", "prefill_partition_size",
     "swap_blocks", "SWAP_OUT", "SWAP_IN",
@@ -51,6 +52,9 @@ EXPORTS = {
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                           _i32, _vp]),
+    "pkv_paged_attention_decode_write": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
+                                                _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
     "pkv_longest_first_order": (_i32, [_P(_i32), _i32, _P(_i32)]),
     "pkv_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_prefill_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -196,6 +200,31 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
         seq_order.data_ptr() if seq_order is not None else None, int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
         ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode")
+
+
+def paged_attention_decode_write(out, q, new_key, new_value, k_cache, v_cache, block_tables,
+                                 context_lens, max_context_len: int, scale: float,
+                                 partition_size: int = PARTITION_AUTO, workspace=None,
+                                 stream=None, seq_order=None) -> None:
+    """The decode step in one launch: sequence b's new token (its last
+    position, ``context_lens[b] - 1``) gets ``new_key[b]`` / ``new_value[b]``
+    (``[B, Hkv, D]``, rows may be strided) written into the caches at the slot
+    its block table gives, then ``paged_attention_decode``."""
+    N, bs, Hkv, D = k_cache.shape
+    B, Hq, _ = q.shape
+    for t, nm in ((new_key, "new_key"), (new_value, "new_value")):
+        if tuple(t.shape) != (B, Hkv, D) or t.stride(2) != 1 or (Hkv > 1 and t.stride(1) != D):
+            raise ValueError(f"paged_attention_decode_write: {nm} must be [{B}, {Hkv}, {D}] "
+                             "with each sequence's row contiguous")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attention_decode_write(
+        out.data_ptr(), q.data_ptr(), new_key.data_ptr(), new_value.data_ptr(),
+        new_key.stride(0) if B else Hkv * D, new_value.stride(0) if B else Hkv * D,
+        k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), seq_order.data_ptr() if seq_order is not None else None,
+        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size), ws_ptr,
+        ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode_write")
 
 
 def upload_pinned(dst, src_pinned, stream=None) -> None:

@@ -31,6 +31,36 @@ namespace pkv {
 namespace {
 
 // ---------------------------------------------------------------------------
+// The decode step's new tokens, for the fused cache write (kernels built with
+// WRITE): sequence b's new token is its last position, ctx_b - 1; its K and V
+// rows (kv heads contiguous, head_dim elements each) start at element
+// b * stride of new_k / new_v.  In the workgroup whose partition holds that
+// position, the first wave of each kv head loads the head's new rows, stores
+// them into the cache at the slot the block table gives and adds the token to
+// its softmax after the chunk loop, which stops one position early: nothing
+// in the launch reads the slot being written.
+struct NewRows {
+  const void* new_k;
+  const void* new_v;
+  int64_t k_stride;  // elements between sequences' rows
+  int64_t v_stride;
+};
+
+// Stores a lane's fragment (the counterpart of load_frag).
+template <int WORDS>
+__device__ __forceinline__ void store_frag(void* p, const Frag<WORDS>& f) {
+  if constexpr (WORDS % 4 == 0) {
+    uint4* v = reinterpret_cast<uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < WORDS / 4; ++i)
+      v[i] = make_uint4(f.w[4 * i + 0], f.w[4 * i + 1], f.w[4 * i + 2], f.w[4 * i + 3]);
+  } else {
+    static_assert(WORDS == 2, "8- or 16-byte multiples only");
+    *reinterpret_cast<uint2*>(p) = make_uint2(f.w[0], f.w[1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Partition kernel, query-head group G on the vector ALUs.
 //
 // HG adjacent kv heads per workgroup (measured on MI355X, LLaMA-13B decode
@@ -38,8 +68,8 @@ namespace {
 // waves reads at 6.34 TB/s: the four waves reading one chunk of four adjacent
 // heads fetch 1 KB contiguous per token row instead of 256 B pieces 10 KB
 // apart).
-template <typename T, int D, int BS, int G, int NW, int HG>
-__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
+template <typename T, int D, int BS, int G, int NW, int HG, bool WRITE>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a, NewRows w) {
   constexpr int EPL = D / 16;                      // elements per lane
   constexpr int WORDS = EPL * int(sizeof(T)) / 4;  // 32-bit words per lane
   constexpr int S = NW / HG;                       // waves (chunk streams) per head
@@ -69,12 +99,34 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
     }
     return;
   }
+  // Fused write: the new token (position `last`) belongs to the workgroup
+  // whose partition holds it.  There the first stream of each head loads the
+  // head's new K/V rows from the input together with q; after the chunk loop,
+  // which stops before the token, it stores them into the cache slot and adds
+  // the token to its softmax: no load of this launch touches the slot being
+  // written.
+  const int last = ctx - 1;
+  const bool own_new = WRITE && last >= t0 && last < t1;
+  const int t1l = own_new ? last : t1;  // end of the chunk loop
+  // The token goes to the stream with the fewest chunks: stream k takes
+  // chunks k, k + S, ... of the partition's n, so stream n % S is one short
+  // unless S divides n.
+  const int n_chunks = (t1l + kChunk - 1) / kChunk - t0 / kChunk;
+  const bool add_new = own_new && stream == n_chunks % S;
 
   // q for the G heads of this kv head, same lane layout as K rows.
   F qf[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
     load_frag(qf[h], static_cast<const T*>(a.q) + (size_t(b) * Hq + kvh * G + h) * D + r * EPL);
+  F kn, vn;  // the new token's rows (every row group holds a copy)
+  if constexpr (WRITE) {
+    if (add_new) {
+      const size_t nrow = size_t(kvh) * D + size_t(r) * EPL;
+      load_frag(kn, static_cast<const T*>(w.new_k) + size_t(b) * w.k_stride + nrow);
+      load_frag(vn, static_cast<const T*>(w.new_v) + size_t(b) * w.v_stride + nrow);
+    }
+  }
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -90,7 +142,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
   const T* vc = static_cast<const T*>(a.v_cache);
   const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
   const int c_begin = t0 / kChunk;
-  const int c_end = (t1 + kChunk - 1) / kChunk;
+  const int c_end = (t1l + kChunk - 1) / kChunk;
 
   // Issues the loads of chunk c.  Every lane loads: slots past t1 re-read the
   // chunk's first row (always inside the context) and are masked to -inf
@@ -115,19 +167,19 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
     const char* vb = reinterpret_cast<const char*>(vc) + rowbase;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = !live ? 0u : (tc + 4 * i + grp < t1 ? slot_off[i] : lane_off);
+      const uint32_t off = !live ? 0u : (tc + 4 * i + grp < t1l ? slot_off[i] : lane_off);
       load_frag_stream(kd[i], kb + off);
       load_frag_stream(vd[i], vb + off);
     }
   };
 
   // Online-softmax update of every query head with chunk c's rows.
-  auto consume = [&](int c, const F (&kd)[4], const F (&vd)[4]) {
-    const int tc = c * kChunk;
+  // Online-softmax update with the rows of tokens tc .. tc+15 below thi.
+  auto consume_at = [&](int tc, int thi, const F (&kd)[4], const F (&vd)[4]) {
     float s[G][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool valid = tc + 4 * i + grp < t1;
+      const bool valid = tc + 4 * i + grp < thi;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.0f;
@@ -169,6 +221,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
     }
   };
 
+  auto consume = [&](int c, const F (&kd)[4], const F (&vd)[4]) {
+    consume_at(c * kChunk, t1l, kd, vd);
+  };
+
   // Two register buffers, alternating.
   F ka[4], va[4], kb2[4], vb2[4];
   int c = c_begin + stream;
@@ -187,6 +243,42 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
       consume(c, kb2, vb2);
       c += S;
       if (c >= c_end) break;
+    }
+  }
+
+  if constexpr (WRITE) {
+    if (add_new) {  // the new token (only slot 0 of row group 0 is below last + 1)
+      // Stored only now: a store right after the loads above would wait for
+      // them before the first chunk's loads could issue.
+      const int bid = tbl[last / BS];
+      if (grp == 0 && (unsigned)bid < (unsigned)a.num_blocks) {
+        const size_t dst = ((size_t(bid) * BS + last % BS) * Hkv + kvh) * D + size_t(r) * EPL;
+        store_frag(const_cast<T*>(kc) + dst, kn);
+        store_frag(const_cast<T*>(vc) + dst, vn);
+      }
+      // Online-softmax update with one row (row group 0's copy; the others
+      // score -inf): the same arithmetic as a chunk whose other slots are
+      // masked, a quarter of the work.
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.0f;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int x = 0; x < WORDS; ++x) d = dot2_bf16(qf[h].w[x], kn.w[x], d);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) d = fmaf(elem<T>(qf[h], e), elem<T>(kn, e), d);
+        }
+        d = row_sum16(d) * a.scale_log2;
+        const float sc = grp == 0 ? d : -INFINITY;
+        const float mn = fmaxf(m[h], sc);
+        const float alpha = fast_exp2(m[h] - mn);
+        const float p = fast_exp2(sc - mn);
+        l[h] = l[h] * alpha + p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, elem<T>(vn, e), acc[h][e] * alpha);
+        m[h] = mn;
+      }
     }
   }
 
@@ -307,8 +399,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a) {
 constexpr bool kMfmaKNT = PKV_MFMA_K_NT;
 constexpr bool kMfmaVNT = PKV_MFMA_V_NT;
 
-template <int D, int BS, int NW, int HG>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
+template <int D, int BS, int NW, int HG, bool WRITE>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRows w) {
   constexpr int KSTEPS = D / 32;  // q.K^T MFMA steps over head_dim
   constexpr int EPL = D / 16;     // V elements per lane per token row = PV tiles
   constexpr int VW = EPL / 2;     // 32-bit words per V load
@@ -346,6 +438,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
         store_elem<uint16_t>(a.out, out_row_of(kvh0, 0) * D + i, 0.0f);
     return;
   }
+  // Fused write: as in the vector kernel, the chunk loop stops before the new
+  // token and the first stream of each head stores it and adds it from the
+  // input.
+  const int last = ctx - 1;
+  const bool own_new = WRITE && last >= t0 && last < t1;
+  const int t1l = own_new ? last : t1;  // end of the chunk loop
+  const int n_chunks = (t1l + kChunk - 1) / kChunk - t0 / kChunk;
+  const bool add_new = own_new && stream == n_chunks % S;  // the stream with the fewest chunks
 
   // Q^T operand: row n (zeros past the valid rows), dims 8c + 32j .. +7.
   uint4 qop[KSTEPS];
@@ -369,7 +469,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
   const char* vc = static_cast<const char*>(a.v_cache);
   const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
   const int c_begin = t0 / kChunk;
-  const int c_end = (t1 + kChunk - 1) / kChunk;
+  const int c_end = (t1l + kChunk - 1) / kChunk;
 
   // Byte offsets inside a chunk: K row of token n (dims 8c + 32j), V row of
   // token 4c + i (dims EPL*n ..).  Masked slots fall back to the chunk's row 0.
@@ -387,6 +487,29 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
     uint4 k[KSTEPS];
     uint32_t v[4][VW];
   };
+  // The new token as the operands of token 0 of a chunk: every lane holds
+  // K dims 8c + 32j and V dims EPL*n of the new rows.
+  uint4 nk[KSTEPS];
+  uint32_t nv[VW];
+  if constexpr (WRITE) {
+    if (add_new) {
+      const char* kn = static_cast<const char*>(w.new_k) + (size_t(b) * w.k_stride + size_t(kvh) * D) * 2;
+      const char* vn = static_cast<const char*>(w.new_v) + (size_t(b) * w.v_stride + size_t(kvh) * D) * 2;
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) nk[j] = load16<false>(kn + kmask[j]);
+      if constexpr (VW == 4) {
+        const uint4 x = load16<false>(vn + vmask);
+        nv[0] = x.x;
+        nv[1] = x.y;
+        nv[2] = x.z;
+        nv[3] = x.w;
+      } else {
+        const uint2 x = load8<false>(vn + vmask);
+        nv[0] = x.x;
+        nv[1] = x.y;
+      }
+    }
+  }
   // `live` false: the branch-free prefetch past a wave's last chunk; every
   // lane then reads the cache's first 16 bytes.
   auto load_chunk = [&](int ch, Regs& r, bool live) {
@@ -397,29 +520,30 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
         live ? ((size_t(bid) * BS + (tc % BS)) * row_stride + size_t(kvh) * D) * 2 : 0;
     const char* kb = kc + rowbase;
     const char* vb = vc + rowbase;
-    const bool kvalid = tc + n < t1;
+    const bool kvalid = tc + n < t1l;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j)
       r.k[j] = load16<kMfmaKNT>(kb + (!live ? 0u : (kvalid ? koff[j] : kmask[j])));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = !live ? 0u : (tc + 4 * c + i < t1 ? voff[i] : vmask);
+      const uint32_t off = !live ? 0u : (tc + 4 * c + i < t1l ? voff[i] : vmask);
+      const char* vsrc = vb + off;
       if constexpr (VW == 4) {
-        const uint4 x = load16<kMfmaVNT>(vb + off);
+        const uint4 x = load16<kMfmaVNT>(vsrc);
         r.v[i][0] = x.x;
         r.v[i][1] = x.y;
         r.v[i][2] = x.z;
         r.v[i][3] = x.w;
       } else {
-        const uint2 x = load8<kMfmaVNT>(vb + off);
+        const uint2 x = load8<kMfmaVNT>(vsrc);
         r.v[i][0] = x.x;
         r.v[i][1] = x.y;
       }
     }
   };
 
-  auto consume = [&](int ch, const Regs& r) {
-    const int tc = ch * kChunk;
+  // Online-softmax update with the rows of tokens tc .. tc+15 below thi.
+  auto consume_at = [&](int tc, int thi, const Regs& r) {
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j)
@@ -430,7 +554,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tc + 4 * c + i;
-      sc[i] = t < t1 ? s[i] * a.scale_log2 : -INFINITY;
+      sc[i] = t < thi ? s[i] * a.scale_log2 : -INFINITY;
     }
     const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if (__ballot(mx > m + kLazyMax)) {  // rare: move the reference max
@@ -466,6 +590,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
     }
   };
 
+  auto consume = [&](int ch, const Regs& r) { consume_at(ch * kChunk, t1l, r); };
+
   constexpr int WSTEP = S;  // chunks between one wave's iterations
   Regs ra, rb;
   int ch = c_begin + stream;
@@ -484,6 +610,35 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a) {
       consume(ch, rb);
       ch += WSTEP;
       if (ch >= c_end) break;
+    }
+  }
+  if constexpr (WRITE) {
+    if (add_new) {  // the new token (only token 0 of the chunk is below last + 1)
+      // Stored after the loop so the first chunk's loads do not wait for it.
+      const int bid = tbl[last / BS];
+      if ((unsigned)bid < (unsigned)a.num_blocks) {
+        const size_t dst = ((size_t(bid) * BS + last % BS) * row_stride + size_t(kvh) * D) * 2;
+        char* kd = const_cast<char*>(kc) + dst;
+        char* vd = const_cast<char*>(vc) + dst;
+        if (n == 0) {  // lanes 0, 16, 32, 48: K dims 8c + 32j
+#pragma unroll
+          for (int j = 0; j < KSTEPS; ++j) *reinterpret_cast<uint4*>(kd + kmask[j]) = nk[j];
+        }
+        if (c == 0) {  // lanes 0 .. 15: V dims EPL*n
+          if constexpr (VW == 4)
+            *reinterpret_cast<uint4*>(vd + vmask) = make_uint4(nv[0], nv[1], nv[2], nv[3]);
+          else
+            *reinterpret_cast<uint2*>(vd + vmask) = make_uint2(nv[0], nv[1]);
+        }
+      }
+      Regs rn;
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) rn.k[j] = nk[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int x = 0; x < VW; ++x) rn.v[i][x] = nv[x];
+      consume_at(last, last + 1, rn);
     }
   }
   // the four lanes of row n hold partial sums of the same reference max
@@ -601,18 +756,20 @@ constexpr int kNW = PKV_DECODE_WAVES;  // waves per workgroup
 constexpr int kValuHG = PKV_VALU_HG;     // adjacent kv heads per workgroup (wide layout)
 constexpr int kValuNW = PKV_VALU_WAVES;  // waves per workgroup (wide layout)
 
-template <typename T, int D, int BS, int G>
-hipError_t launch_valu(const AttnArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
+template <bool WRITE, typename T, int D, int BS, int G>
+hipError_t launch_valu(const AttnArgs& a, const NewRows& w, int num_seqs, hipStream_t st,
+                       int grid_parts) {
   if constexpr (sizeof(T) == 2 && G <= 2) {
     if (a.num_kv_heads % 4 == 0) {  // wide_layout() decides the same
       const dim3 grid = work_grid(grid_parts, a.num_kv_heads / kValuHG, num_seqs);
-      hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kValuNW, kValuHG>), grid,
-                         dim3(kValuNW * 64), 0, st, a);
+      hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kValuNW, kValuHG, WRITE>), grid,
+                         dim3(kValuNW * 64), 0, st, a, w);
       return hipGetLastError();
     }
   }
   const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kNW, 1>), grid, dim3(kNW * 64), 0, st, a);
+  hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kNW, 1, WRITE>), grid, dim3(kNW * 64), 0, st,
+                     a, w);
   return hipGetLastError();
 }
 
@@ -625,15 +782,17 @@ hipError_t launch_valu(const AttnArgs& a, int num_seqs, hipStream_t st, int grid
 constexpr int kMfmaHG = PKV_MFMA_HG;     // adjacent kv heads per workgroup
 constexpr int kMfmaNW = PKV_MFMA_WAVES;  // waves per workgroup
 
-template <int D, int BS>
-hipError_t launch_mfma(const AttnArgs& a, int num_seqs, hipStream_t st, int grid_parts) {
+template <bool WRITE, int D, int BS>
+hipError_t launch_mfma(const AttnArgs& a, const NewRows& w, int num_seqs, hipStream_t st,
+                       int grid_parts) {
   if (kMfmaHG > 1 && a.num_kv_heads % kMfmaHG == 0) {
     const dim3 grid = work_grid(grid_parts, a.num_kv_heads / kMfmaHG, num_seqs);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kMfmaNW, kMfmaHG>), grid, dim3(kMfmaNW * 64), 0,
-                       st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kMfmaNW, kMfmaHG, WRITE>), grid,
+                       dim3(kMfmaNW * 64), 0, st, a, w);
   } else {
     const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW, 1>), grid, dim3(kNW * 64), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW, 1, WRITE>), grid, dim3(kNW * 64), 0, st, a,
+                       w);
   }
   return hipGetLastError();
 }
@@ -671,26 +830,37 @@ int32_t decode_partition(bool bf16, int32_t num_q_heads, int32_t num_kv_heads,
   return resolve_partition(max_context_len, partition_size);
 }
 
-template <typename T, int D, int BS>
-hipError_t dispatch_group(const AttnArgs& a, int G, int num_seqs, hipStream_t st,
-                          int grid_parts) {
+template <bool WRITE, typename T, int D, int BS>
+hipError_t dispatch_group(const AttnArgs& a, const NewRows& w, int G, int num_seqs,
+                          hipStream_t st, int grid_parts) {
   if constexpr (sizeof(T) == 2) {
-    if (use_mfma(true, G)) return launch_mfma<D, BS>(a, num_seqs, st, grid_parts);
+    if (use_mfma(true, G)) return launch_mfma<WRITE, D, BS>(a, w, num_seqs, st, grid_parts);
   }
   switch (G) {
-    case 1: return launch_valu<T, D, BS, 1>(a, num_seqs, st, grid_parts);
-    case 2: return launch_valu<T, D, BS, 2>(a, num_seqs, st, grid_parts);
-    case 4: return launch_valu<T, D, BS, 4>(a, num_seqs, st, grid_parts);
-    case 8: return launch_valu<T, D, BS, 8>(a, num_seqs, st, grid_parts);
+    case 1: return launch_valu<WRITE, T, D, BS, 1>(a, w, num_seqs, st, grid_parts);
+    case 2: return launch_valu<WRITE, T, D, BS, 2>(a, w, num_seqs, st, grid_parts);
+    case 4: return launch_valu<WRITE, T, D, BS, 4>(a, w, num_seqs, st, grid_parts);
+    case 8: return launch_valu<WRITE, T, D, BS, 8>(a, w, num_seqs, st, grid_parts);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, int D>
-hipError_t dispatch_bs(const AttnArgs& a, int BS, int G, int num_seqs, hipStream_t st,
-                       int grid_parts) {
-  return BS == 16 ? dispatch_group<T, D, 16>(a, G, num_seqs, st, grid_parts)
-                  : dispatch_group<T, D, 32>(a, G, num_seqs, st, grid_parts);
+template <bool WRITE, typename T, int D>
+hipError_t dispatch_bs(const AttnArgs& a, const NewRows& w, int BS, int G, int num_seqs,
+                       hipStream_t st, int grid_parts) {
+  return BS == 16 ? dispatch_group<WRITE, T, D, 16>(a, w, G, num_seqs, st, grid_parts)
+                  : dispatch_group<WRITE, T, D, 32>(a, w, G, num_seqs, st, grid_parts);
+}
+
+// Every (element type, head_dim) of the attention kernels.
+template <bool WRITE>
+hipError_t dispatch_all(const AttnArgs& a, const NewRows& w, bool f32, int head_dim, int BS,
+                        int G, int num_seqs, hipStream_t st, int grid_parts) {
+  if (head_dim == 64)
+    return f32 ? dispatch_bs<WRITE, float, 64>(a, w, BS, G, num_seqs, st, grid_parts)
+               : dispatch_bs<WRITE, uint16_t, 64>(a, w, BS, G, num_seqs, st, grid_parts);
+  return f32 ? dispatch_bs<WRITE, float, 128>(a, w, BS, G, num_seqs, st, grid_parts)
+             : dispatch_bs<WRITE, uint16_t, 128>(a, w, BS, G, num_seqs, st, grid_parts);
 }
 
 template <typename T, int D>
@@ -737,48 +907,53 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
                                                   max_context_len, partition_size));
 }
 
-extern "C" pkv_status pkv_paged_attention_decode(
-    void* out, const void* q, const void* k_cache, const void* v_cache,
-    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-    void* stream) {
+namespace {
+
+// Decode, optionally with the step's new tokens written first (w non-null):
+// the argument checks, partition choice and launches of both entry points.
+pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, float scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       pkv_dtype dtype, void* stream, const pkv::NewRows* w) {
   if (dtype != PKV_F32 && dtype != PKV_BF16)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: unknown dtype %d", int(dtype));
+    return fail(PKV_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dtype));
   if (num_seqs < 0 || num_seqs > 65535)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: num_seqs=%d outside [0, 65535]",
+    return fail(PKV_ERR_INVALID_ARG, "%s: num_seqs=%d outside [0, 65535]", fn,
                 num_seqs);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_kv_heads > 65535 ||
       num_q_heads % num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode: num_q_heads=%d must be a positive multiple of "
-                "num_kv_heads=%d", num_q_heads, num_kv_heads);
+                "%s: num_q_heads=%d must be a positive multiple of "
+                "num_kv_heads=%d", fn, num_q_heads, num_kv_heads);
   const int G = num_q_heads / num_kv_heads;
   if (head_dim != 64 && head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: head_dim=%d (64 or 128)", head_dim);
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim=%d (64 or 128)", fn, head_dim);
   if (block_size != 16 && block_size != 32)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: block_size=%d (16 or 32)",
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size=%d (16 or 32)", fn,
                 block_size);
   if (!pkv::group_supported(dtype == PKV_BF16, G))
     return fail(PKV_ERR_UNSUPPORTED,
-                "paged_attention_decode: query heads per kv head = %d (1..16 for bf16; "
-                "1, 2, 4 or 8 for f32)", G);
+                "%s: query heads per kv head = %d (1..16 for bf16; "
+                "1, 2, 4 or 8 for f32)", fn, G);
   if (num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
       max_context_len > (1 << 29))
     return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode: num_blocks=%d max_blocks_per_seq=%d "
-                "max_context_len=%d", num_blocks, max_blocks_per_seq, max_context_len);
+                "%s: num_blocks=%d max_blocks_per_seq=%d "
+                "max_context_len=%d", fn, num_blocks, max_blocks_per_seq, max_context_len);
   if (int64_t(num_seqs) * max_blocks_per_seq > INT32_MAX)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: block table too large");
+    return fail(PKV_ERR_INVALID_ARG, "%s: block table too large", fn);
   if (partition_size < PKV_PARTITION_AUTO ||
       (partition_size > 0 && partition_size % block_size != 0))
     return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode: partition_size=%d must be 0, -1 or a multiple of "
-                "block_size=%d", partition_size, block_size);
+                "%s: partition_size=%d must be 0, -1 or a multiple of "
+                "block_size=%d", fn, partition_size, block_size);
   if (num_seqs == 0) return pkv::ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: NULL pointer argument");
+    return fail(PKV_ERR_INVALID_ARG, "%s: NULL pointer argument", fn);
 
   const int32_t partition = pkv::decode_partition(dtype == PKV_BF16, num_q_heads, num_kv_heads,
                                                   max_context_len, partition_size);
@@ -805,7 +980,7 @@ extern "C" pkv_status pkv_paged_attention_decode(
                                            partition);
     if (need > 0 && (!workspace || workspace_bytes < need))
       return fail(PKV_ERR_WORKSPACE,
-                  "paged_attention_decode: workspace of %zu bytes needed, %zu given", need,
+                  "%s: workspace of %zu bytes needed, %zu given", fn, need,
                   workspace ? workspace_bytes : size_t(0));
     a.partition = partition;
     // the workspace is sized from max_context_len; partitions past the clamped
@@ -819,7 +994,7 @@ extern "C" pkv_status pkv_paged_attention_decode(
     if (grid_parts < 1) grid_parts = 1;
     if (grid_parts > 65535)
       return fail(PKV_ERR_INVALID_ARG,
-                  "paged_attention_decode: %d partitions of %d tokens exceed the grid limit",
+                  "%s: %d partitions of %d tokens exceed the grid limit", fn,
                   grid_parts, partition);
   } else {
     a.partition = pkv::kSingle;
@@ -827,15 +1002,11 @@ extern "C" pkv_status pkv_paged_attention_decode(
   }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
   const bool f32 = dtype == PKV_F32;
-  if (head_dim == 64) {
-    e = f32 ? pkv::dispatch_bs<float, 64>(a, block_size, G, num_seqs, st, grid_parts)
-            : pkv::dispatch_bs<uint16_t, 64>(a, block_size, G, num_seqs, st, grid_parts);
-  } else {
-    e = f32 ? pkv::dispatch_bs<float, 128>(a, block_size, G, num_seqs, st, grid_parts)
-            : pkv::dispatch_bs<uint16_t, 128>(a, block_size, G, num_seqs, st, grid_parts);
-  }
+  hipError_t e =
+      w ? pkv::dispatch_all<true>(a, *w, f32, head_dim, block_size, G, num_seqs, st, grid_parts)
+        : pkv::dispatch_all<false>(a, pkv::NewRows{}, f32, head_dim, block_size, G, num_seqs, st,
+                                   grid_parts);
   if (e == hipSuccess && partition > 0) {
     if (head_dim == 64)
       e = f32 ? pkv::launch_reduce<float, 64>(a, num_seqs, st)
@@ -845,6 +1016,48 @@ extern "C" pkv_status pkv_paged_attention_decode(
               : pkv::launch_reduce<uint16_t, 128>(a, num_seqs, st);
   }
   if (e != hipSuccess)
-    return fail(PKV_ERR_HIP, "paged_attention_decode: launch failed: %s", hipGetErrorString(e));
+    return fail(PKV_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return pkv::ok();
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attention_decode(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+    void* stream) {
+  return decode_call("paged_attention_decode", out, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     partition_size, workspace, workspace_bytes, dtype, stream, nullptr);
+}
+
+extern "C" pkv_status pkv_paged_attention_decode_write(
+    void* out, const void* q, const void* new_key, const void* new_value,
+    int64_t key_seq_stride, int64_t value_seq_stride, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+    void* stream) {
+  const int64_t esize = dtype == PKV_F32 ? 4 : 2;
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if (num_seqs > 0 && (!new_key || !new_value))
+    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode_write: NULL new key/value");
+  if (key_seq_stride < row || value_seq_stride < row || (key_seq_stride * esize) % 16 ||
+      (value_seq_stride * esize) % 16 || (reinterpret_cast<uintptr_t>(new_key) & 15u) ||
+      (reinterpret_cast<uintptr_t>(new_value) & 15u) ||
+      (reinterpret_cast<uintptr_t>(k_cache) & 15u) || (reinterpret_cast<uintptr_t>(v_cache) & 15u))
+    return fail(PKV_ERR_INVALID_ARG,
+                "paged_attention_decode_write: sequence strides (%lld, %lld) must be >= %lld "
+                "elements and multiples of 16 bytes, pointers 16-byte aligned",
+                (long long)key_seq_stride, (long long)value_seq_stride, (long long)row);
+  const pkv::NewRows w{new_key, new_value, key_seq_stride, value_seq_stride};
+  return decode_call("paged_attention_decode_write", out, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     partition_size, workspace, workspace_bytes, dtype, stream, &w);
 }
