@@ -36,10 +36,17 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   constexpr int EPL = D / 16;
   constexpr int VW = EPL / 2;
   constexpr int RB = D * 2;            // bytes of one token's K (or V) row
-  constexpr int PITCH = RB + 16;       // padded LDS row pitch
+  // LDS row pitches (bytes), chosen from measured ds_read_b128 bank
+  // conflicts on gfx950 for 256-byte rows: the K operand read (lane (c, n):
+  // row n, bytes 16c + 64j) is conflict-free at a 288-byte pitch and takes
+  // twice as long at 272; the V operand read (rows 4c + i, bytes 16n) is
+  // conflict-free unpadded.  The chunk stores run at full write rate on both.
+  constexpr int PITCH_K = D == 128 ? RB + 32 : RB + 16;
+  constexpr int PITCH_V = D == 128 ? RB : RB + 16;
   constexpr int LPR = RB / 16;         // 16-byte pieces per row
   constexpr int PIECES = 16 * LPR;     // pieces per 16-token chunk, per cache
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2][16 * PITCH];  // [buffer][K/V]
+  __shared__ __attribute__((aligned(16))) char s_k[2][16 * PITCH_K];  // [buffer]
+  __shared__ __attribute__((aligned(16))) char s_v[2][16 * PITCH_V];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -159,7 +166,8 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
       const int p = threadIdx.x + k * NWP * 64;
       if (p < 2 * PIECES) {
         const int pp = p % PIECES;
-        *reinterpret_cast<uint4*>(&s_kv[buf][p < PIECES ? 0 : 1][(pp / LPR) * PITCH + 16 * (pp % LPR)]) = stage[k];
+        char* dst = p < PIECES ? &s_k[buf][(pp / LPR) * PITCH_K] : &s_v[buf][(pp / LPR) * PITCH_V];
+        *reinterpret_cast<uint4*>(dst + 16 * (pp % LPR)) = stage[k];
       }
     }
   };
@@ -167,8 +175,8 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   auto compute = [&](int ch, int buf) {
     const int tc = ch * kChunk;
     if (tc >= t1_max) return;  // none of this wave's tiles sees a token of this chunk
-    const char* ks = s_kv[buf][0];
-    const char* vs = s_kv[buf][1];
+    const char* ks = s_k[buf];
+    const char* vs = s_v[buf];
     // S^T = K . Q^T for every tile, each K operand read once
     f32x4_t s[TPW];
 #pragma unroll
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
       const bf16x8_t kop =
-          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ks + n * PITCH + 16 * c + 64 * j));
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ks + n * PITCH_K + 16 * c + 64 * j));
 #pragma unroll
       for (int u = 0; u < TPW; ++u)
         s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, __builtin_bit_cast(bf16x8_t, qop[u][j]),
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
     uint32_t v[4][VW];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const char* src = vs + (4 * c + i) * PITCH + EPL * 2 * n;
+      const char* src = vs + (4 * c + i) * PITCH_V + EPL * 2 * n;
       if constexpr (VW == 4) {
         const uint4 x = *reinterpret_cast<const uint4*>(src);
         v[i][0] = x.x;
