@@ -207,18 +207,15 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
         v[i][1] = x.y;
       }
     }
+    // element t of two rows into one word: a byte permute per word (bytes
+    // 0-1 of the first row's word, then of the second's; 2-3 for odd t)
     s16x4_t vb[EPL];
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
       const int w = t >> 1;
-      uint32_t lo, hi;
-      if (t & 1) {
-        lo = (v[0][w] >> 16) | (v[1][w] & 0xFFFF0000u);
-        hi = (v[2][w] >> 16) | (v[3][w] & 0xFFFF0000u);
-      } else {
-        lo = (v[0][w] & 0xFFFFu) | (v[1][w] << 16);
-        hi = (v[2][w] & 0xFFFFu) | (v[3][w] << 16);
-      }
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
       vb[t] = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
     }
 #pragma unroll
