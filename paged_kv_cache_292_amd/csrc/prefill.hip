@@ -34,15 +34,14 @@ template <int D, int BS, int NWP, int TPW>
 __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 32;
   constexpr int EPL = D / 16;
-  constexpr int VW = EPL / 2;
   constexpr int RB = D * 2;            // bytes of one token's K (or V) row
-  // LDS row pitches (bytes), chosen from measured ds_read_b128 bank
-  // conflicts on gfx950 for 256-byte rows: the K operand read (lane (c, n):
-  // row n, bytes 16c + 64j) is conflict-free at a 288-byte pitch and takes
-  // twice as long at 272; the V operand read (rows 4c + i, bytes 16n) is
-  // conflict-free unpadded.  The chunk stores run at full write rate on both.
+  // LDS row pitch (bytes), chosen from measured bank conflicts on gfx950
+  // for 256-byte rows: at 288 bytes both operand reads are conflict-free —
+  // the K read (ds_read_b128, lane (c, n): row n, bytes 16c + 64j; twice as
+  // long at 272) and the transposing V read (ds_read_b64_tr_b16, rows 4c +
+  // k/4; 8x as long unpadded) — and the chunk stores run at full write rate.
   constexpr int PITCH_K = D == 128 ? RB + 32 : RB + 16;
-  constexpr int PITCH_V = D == 128 ? RB : RB + 16;
+  constexpr int PITCH_V = PITCH_K;
   constexpr int LPR = RB / 16;         // 16-byte pieces per row
   constexpr int PIECES = 16 * LPR;     // pieces per 16-token chunk, per cache
   __shared__ __attribute__((aligned(16))) char s_k[2][16 * PITCH_K];  // [buffer]
@@ -190,33 +189,19 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
         s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, __builtin_bit_cast(bf16x8_t, qop[u][j]),
                                                        s[u], 0, 0, 0);
     }
-    // V^T operands: element t of rows 4c..4c+3 (dims EPL*n ..), packed once
-    uint32_t v[4][VW];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* src = vs + (4 * c + i) * PITCH_V + EPL * 2 * n;
-      if constexpr (VW == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(src);
-        v[i][0] = x.x;
-        v[i][1] = x.y;
-        v[i][2] = x.z;
-        v[i][3] = x.w;
-      } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(src);
-        v[i][0] = x.x;
-        v[i][1] = x.y;
-      }
-    }
-    // element t of two rows into one word: a byte permute per word (bytes
-    // 0-1 of the first row's word, then of the second's; 2-3 for odd t)
+    // V^T operand of output tile t (dims 16t .. 16t+15) for tokens 4c ..
+    // 4c+3, straight from LDS with the transposing read: in each 16-lane
+    // group, lane k reads 8 bytes of row 4c + k/4 at dims 16t + 4(k%4), and
+    // lane j receives element j%4 of the reads of lanes j/4, j/4 + 4, + 8,
+    // + 12, i.e. dim 16t + j of rows 4c .. 4c+3.
     s16x4_t vb[EPL];
+    {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      const char* vrow = vs + (4 * c + (n >> 2)) * PITCH_V + 8 * (n & 3);
 #pragma unroll
-    for (int t = 0; t < EPL; ++t) {
-      const int w = t >> 1;
-      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t lo = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
-      vb[t] = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
+      for (int t = 0; t < EPL; ++t)
+        vb[t] = __builtin_bit_cast(s16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                (__attribute__((address_space(3))) v4s*)(vrow + 32 * t)));
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -304,7 +289,7 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int t = 0; t < EPL; ++t) {
-          const int d = EPL * (4 * c + r) + t;
+          const int d = 16 * t + 4 * c + r;  // row 4c + r of output tile t
           const float o = lu > 0.0f ? acc[u][t][r] / lu : 0.0f;
           if (single) {
             store_elem<uint16_t>(a.out, out_row(u, n) * D + d, o);
