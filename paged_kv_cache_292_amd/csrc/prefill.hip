@@ -22,14 +22,15 @@ namespace {
 // head, partition); a tile is 16 (query, head) rows, floor(16 / G)
 // consecutive queries times the G query heads of the kv head, the 16 operand
 // columns of the matrix products (the decode kernel's layout, with queries
-// added), and each wave owns TPW consecutive tiles.  Each 16-token K/V chunk
+// added), and each wave owns TPW consecutive tiles.  Each 32-token K/V chunk
 // is loaded once by the whole workgroup — whole rows, streamed — into a
 // double-buffered LDS tile; every wave reads each K and V operand from LDS
-// once and uses it for all of its tiles (LDS reads per flop fall with TPW),
-// and packs the V operand once for all of them.  The next chunk's loads are
-// in flight while the current one is computed.  Tiles that see no token of a
-// chunk (the causal boundary) skip its math; their waves keep to the
-// barriers.
+// once and uses it for all of its tiles (LDS reads per flop fall with TPW).
+// Both products are 32-deep matrix instructions: q.K^T over head_dim, and
+// P.V over the chunk's 32 tokens, its V operand read transposed from LDS.
+// The next chunks' loads are in flight while the current one is computed.
+// Tiles that see no token of a chunk (the causal boundary) skip its math;
+// their waves keep to the barriers.
 template <int D, int BS, int NWP, int TPW>
 __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 32;
@@ -42,10 +43,13 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   // k/4; 8x as long unpadded) — and the chunk stores run at full write rate.
   constexpr int PITCH_K = D == 128 ? RB + 32 : RB + 16;
   constexpr int PITCH_V = PITCH_K;
+  constexpr int CH = 32;               // tokens per K/V chunk (one barrier each)
+  constexpr int NBC = CH / BS;         // cache blocks per chunk
+  static_assert(CH % BS == 0, "a chunk covers whole blocks");
   constexpr int LPR = RB / 16;         // 16-byte pieces per row
-  constexpr int PIECES = 16 * LPR;     // pieces per 16-token chunk, per cache
-  __shared__ __attribute__((aligned(16))) char s_k[2][16 * PITCH_K];  // [buffer]
-  __shared__ __attribute__((aligned(16))) char s_v[2][16 * PITCH_V];
+  constexpr int PIECES = CH * LPR;     // pieces per chunk, per cache
+  __shared__ __attribute__((aligned(16))) char s_k[2][CH * PITCH_K];  // [buffer]
+  __shared__ __attribute__((aligned(16))) char s_v[2][CH * PITCH_V];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -127,36 +131,55 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
   const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
-  const int c_begin = t0 / kChunk;
-  const int c_end = (g_t1 + kChunk - 1) / kChunk;
+  const int c_begin = t0 / CH;
+  const int c_end = (g_t1 + CH - 1) / CH;
 
   // Cooperative chunk load: piece p (< 2 * PIECES) of the chunk is 16 bytes of
   // K (p < PIECES) or V, token p % PIECES / LPR, bytes 16 * (p % LPR).
   constexpr int PER_LANE = (2 * PIECES + NWP * 64 - 1) / (NWP * 64);
   using Stage = uint4[PER_LANE];
+  // Per piece, the parts of its address that do not change from chunk to
+  // chunk: the cache, the block of the chunk it falls in, and its byte offset
+  // inside that block (and the same for the chunk's first row, which pieces
+  // past the end of the range re-read).
+  const char* pbase[PER_LANE];
+  int ptok[PER_LANE];
+  uint32_t poff[PER_LANE], poff0[PER_LANE];
+#pragma unroll
+  for (int k = 0; k < PER_LANE; ++k) {
+    // every lane loads (lanes past the chunk's pieces re-read piece 0 and
+    // store nothing), so no lane-masked branch hides the loads from the
+    // compiler's wait-count tracking
+    const int p0 = threadIdx.x + k * NWP * 64;
+    const int p = p0 < 2 * PIECES ? p0 : 0;
+    const int pp = p % PIECES;
+    ptok[k] = pp / LPR;
+    pbase[k] = p < PIECES ? kc : vc;
+    poff0[k] = uint32_t((size_t(kvh) * D) * 2 + 16 * (pp % LPR));
+    poff[k] = poff0[k] + uint32_t((ptok[k] % BS) * row_stride * 2);
+  }
   // `live` false: the prefetch past the last chunk, issued anyway so that no
   // branch hides the loads from the wait-count tracking; every lane then
   // reads the cache's first 16 bytes (one line per wave).
   auto fetch = [&](int ch, Stage& stage, bool live) {
-    const int tc = __builtin_amdgcn_readfirstlane(ch * kChunk);
-    int bid = scalar_read(tbl + tc / BS);
-    bid = (unsigned)bid < (unsigned)a.num_blocks ? bid : 0;
-    const size_t rowbase =
-        live ? ((size_t(bid) * BS + (tc % BS)) * row_stride + size_t(kvh) * D) * 2 : 0;
+    const int tc = __builtin_amdgcn_readfirstlane(ch * CH);
+    // the chunk's blocks (entries past the range repeat its first block, so
+    // no table entry beyond the context is read)
+    const int last_blk = (g_t1 - 1) / BS;
+    size_t blk[NBC];
+#pragma unroll
+    for (int j = 0; j < NBC; ++j) {
+      int bid = scalar_read(tbl + min(tc / BS + j, last_blk));
+      bid = (unsigned)bid < (unsigned)a.num_blocks ? bid : 0;
+      blk[j] = live ? size_t(bid) * BS * row_stride * 2 : 0;
+    }
 #pragma unroll
     for (int k = 0; k < PER_LANE; ++k) {
-      // every lane loads (lanes past the chunk's pieces re-read piece 0 and
-      // store nothing), so no lane-masked branch hides the loads from the
-      // compiler's wait-count tracking
-      const int p0 = threadIdx.x + k * NWP * 64;
-      const int p = p0 < 2 * PIECES ? p0 : 0;
-      const int pp = p % PIECES;
-      const int tok = pp / LPR;
-      const char* base = (p < PIECES ? kc : vc) + rowbase;
       // rows past the range re-read the chunk's first row (masked later)
-      const uint32_t off =
-          !live ? 0u : uint32_t((tc + tok < g_t1 ? tok * row_stride * 2 : 0) + 16 * (pp % LPR));
-      stage[k] = load16<true>(base + off);
+      const bool in = tc + ptok[k] < g_t1;
+      const size_t b0 = NBC > 1 && in ? blk[ptok[k] / BS] : blk[0];
+      const uint32_t off = !live ? 0u : (in ? poff[k] : poff0[k]);
+      stage[k] = load16<true>(pbase[k] + b0 + off);
     }
   };
   auto store = [&](int buf, const Stage& stage) {
@@ -172,52 +195,49 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   };
 
   auto compute = [&](int ch, int buf) {
-    const int tc = ch * kChunk;
+    const int tc = ch * CH;
     if (tc >= t1_max) return;  // none of this wave's tiles sees a token of this chunk
     const char* ks = s_k[buf];
     const char* vs = s_v[buf];
-    // S^T = K . Q^T for every tile, each K operand read once
-    f32x4_t s[TPW];
+    // S^T = K . Q^T for every tile and each 16-token half h of the chunk,
+    // each K operand read once
+    f32x4_t s[TPW][2];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) s[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < TPW; ++u) s[u][0] = s[u][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      const bf16x8_t kop =
-          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ks + n * PITCH_K + 16 * c + 64 * j));
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int u = 0; u < TPW; ++u)
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, __builtin_bit_cast(bf16x8_t, qop[u][j]),
-                                                       s[u], 0, 0, 0);
-    }
-    // V^T operand of output tile t (dims 16t .. 16t+15) for tokens 4c ..
-    // 4c+3, straight from LDS with the transposing read: in each 16-lane
-    // group, lane k reads 8 bytes of row 4c + k/4 at dims 16t + 4(k%4), and
-    // lane j receives element j%4 of the reads of lanes j/4, j/4 + 4, + 8,
-    // + 12, i.e. dim 16t + j of rows 4c .. 4c+3.
-    s16x4_t vb[EPL];
-    {
-      typedef short v4s __attribute__((ext_vector_type(4)));
-      const char* vrow = vs + (4 * c + (n >> 2)) * PITCH_V + 8 * (n & 3);
+      for (int j = 0; j < KSTEPS; ++j) {
+        const bf16x8_t kop = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(ks + (16 * h + n) * PITCH_K + 16 * c + 64 * j));
 #pragma unroll
-      for (int t = 0; t < EPL; ++t)
-        vb[t] = __builtin_bit_cast(s16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                (__attribute__((address_space(3))) v4s*)(vrow + 32 * t)));
-    }
+        for (int u = 0; u < TPW; ++u)
+          s[u][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kop, __builtin_bit_cast(bf16x8_t, qop[u][j]), s[u][h], 0, 0, 0);
+      }
+    bf16x8_t pb[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (tc >= t1[u]) continue;  // wave-uniform
-      float sc[4];
-      if (tc + kChunk <= t1[u] && tc + kChunk - 1 <= pos_lo[u]) {  // every row sees every token
+      // sc[4h + i]: token tc + 16h + 4c + i of query row n
+      float sc[8];
+      if (tc >= t0 && tc + CH <= t1[u] && tc + CH - 1 <= pos_lo[u]) {  // every row sees every token
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = s[u][i] * a.scale_log2;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[4 * h + i] = s[u][h][i] * a.scale_log2;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tc + 4 * c + i;
-          sc[i] = (t < t1[u] && t <= pos_n[u]) ? s[u][i] * a.scale_log2 : -INFINITY;
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = tc + 16 * h + 4 * c + i;
+            sc[4 * h + i] =
+                (t >= t0 && t < t1[u] && t <= pos_n[u]) ? s[u][h][i] * a.scale_log2 : -INFINITY;
+          }
       }
-      const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
       if (__ballot(mx > m[u] + kLazyMax)) {
         float hm = fmaxf(mx, __shfl_xor(mx, 16));
         hm = fmaxf(hm, __shfl_xor(hm, 32));
@@ -228,15 +248,36 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
         for (int t = 0; t < EPL; ++t) acc[u][t] *= alpha;
         m[u] = mn;
       }
-      float p[4];
+      float p[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m[u]);
-      l[u] += (p[0] + p[1]) + (p[2] + p[3]);
-      const s16x4_t pb = __builtin_bit_cast(
-          s16x4_t, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sc[i] - m[u]);
+      l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pb[u] = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+    }
+    // O^T += V^T . P^T, tile by tile (one tile's V operand live at a time).
+    // The V^T operand of output tile t (dims 16t .. 16t+15) over the chunk's
+    // 32 tokens has k-slots 8c .. 8c+7 = tokens 4c .. 4c+3 and 16+4c ..
+    // 16+4c+3, the tokens whose scores lane (c, n) holds.  It comes straight
+    // from LDS with the transposing read: in each 16-lane group, lane k reads
+    // 8 bytes of row r0 + k/4 at dims 16t + 4(k%4), and lane j receives
+    // element j%4 of the reads of lanes j/4, j/4 + 4, + 8, + 12, i.e. dim
+    // 16t + j of rows r0 .. r0+3.
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const char* vrow = vs + (4 * c + (n >> 2)) * PITCH_V + 8 * (n & 3);
 #pragma unroll
-      for (int t = 0; t < EPL; ++t)
-        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb[t], pb, acc[u][t], 0, 0, 0);
+    for (int t = 0; t < EPL; ++t) {
+      const uint2 lo =
+          __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 32 * t)));
+      const uint2 hi = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 16 * PITCH_V + 32 * t)));
+      const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        if (tc < t1[u])
+          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u], acc[u][t], 0, 0, 0);
     }
   };
 
@@ -245,7 +286,8 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   // computed, so four chunks are in flight per workgroup.  With one chunk in
   // flight the loads, not the math, set the pace (measured: 2.3x slower than
   // the same kernel without global loads): a workgroup needs tens of KB in
-  // flight to cover the memory latency.  Four register stages rotate; two LDS
+  // flight to cover the memory latency (four 32-token chunks are 64 KB per
+  // workgroup at head_dim 128).  Four register stages rotate; two LDS
   // buffers alternate by the chunk's parity; one barrier per chunk.  The loop
   // starts four chunks early (those steps only fetch and store), so every
   // fetch comes from the same loop body.

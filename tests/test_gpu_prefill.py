@@ -142,3 +142,19 @@ def test_prefill_tile_before_the_context_start_next_to_live_tiles():
                            "bf16")
     assert (got[:40] == 0).all()
     assert_close(got, ref, "bf16", "tile before position 0")
+
+
+@pytest.mark.parametrize("case", [0, 2, 3, 5])
+@pytest.mark.parametrize("part", [16, 48])
+def test_prefill_partitions_that_start_inside_a_chunk(case, part):
+    """Partitions of 16 or 48 tokens (multiples of the block size, not of the
+    kernel's 32-token K/V chunk): every other partition starts in the middle
+    of a chunk, whose first half belongs to the previous partition."""
+    prior, chunks, Hq, Hkv, D, bs = CASES[case]
+    log(f"prefill case {case} partition={part} (starts inside a chunk)")
+    cs = _prefill_case(prior, chunks, Hq, Hkv, D, bs, seed=400 + case)
+    scale = 1.0 / np.sqrt(D)
+    got = _run(cs, Hq, D, part, scale)
+    ref = OA.paged_prefill(cs["q"], cs["ko"], cs["vo"], cs["tables"], cs["ctx"], cs["starts"],
+                           scale, "bf16")
+    assert_close(got, ref, "bf16", f"prefill case {case} p{part}")
