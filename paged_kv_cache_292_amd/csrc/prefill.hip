@@ -218,7 +218,10 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
     bf16x8_t pb[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      if (tc >= t1[u]) continue;  // wave-uniform
+      if (tc >= t1[u]) {  // wave-uniform: the tile adds nothing (every V row in LDS is finite)
+        pb[u] = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+        continue;
+      }
       // sc[4h + i]: token tc + 16h + 4c + i of query row n
       float sc[8];
       if (tc >= t0 && tc + CH <= t1[u] && tc + CH - 1 <= pos_lo[u]) {  // every row sees every token
@@ -276,8 +279,7 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
       const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
       for (int u = 0; u < TPW; ++u)
-        if (tc < t1[u])
-          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u], acc[u][t], 0, 0, 0);
+        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u], acc[u][t], 0, 0, 0);
     }
   };
 
@@ -390,15 +392,15 @@ __global__ __launch_bounds__(256) void merge_prefill_kernel(AttnArgs a) {
 // Host side.
 
 
-// Measured on MI355X (16 sequences x 40 heads, 512-token chunks): 16 waves x
-// 1 tile 475 TFLOP/s, 8 x 2 409, 4 x 2 361, 4 x 4 262 — more tiles per wave
-// halve the LDS reads per flop but lengthen each wave's dependent chain
-// between the per-chunk barriers, which costs more.
+// Measured on MI355X (16 sequences x 40 heads, 512-token chunks, contexts
+// to 31K): 8 waves x 2 tiles 774 TFLOP/s, 16 x 1 742, 8 x 1 556, 4 x 4 496.
+// Two tiles per wave share each K and V operand read from LDS; 16 tiles per
+// workgroup share each K/V chunk read from memory.
 #ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 16
+#define PKV_PREFILL_WAVES 8
 #endif
 #ifndef PKV_PREFILL_TPW
-#define PKV_PREFILL_TPW 1
+#define PKV_PREFILL_TPW 2
 #endif
 constexpr int kPrefillNW = PKV_PREFILL_WAVES;  // waves per workgroup, long chunks
 constexpr int kPrefillTPW = PKV_PREFILL_TPW;   // query tiles per wave, long chunks
