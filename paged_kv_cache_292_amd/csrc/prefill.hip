@@ -12,6 +12,11 @@
 // through LDS.
 #include "attn_common.h"
 
+// Register stages of the K/V prefetch (chunks in flight per workgroup; even).
+#ifndef PKV_PREFILL_STAGES
+#define PKV_PREFILL_STAGES 4
+#endif
+
 namespace pkv {
 namespace {
 
@@ -296,8 +301,9 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   // the query operands (loaded above) are complete before the pipeline
   // starts, so no wait inside it has to cover them
   __builtin_amdgcn_s_waitcnt(0);
-  constexpr int NST = 4;
-  Stage st0, st1, st2, st3;
+  constexpr int NST = PKV_PREFILL_STAGES;
+  static_assert(NST % 2 == 0, "chunk x uses LDS buffer (x - c_begin) % 2 in every round");
+  Stage st[NST];
   // step of chunk x (its register stage `mine`, the next chunk's `next`)
   auto step = [&](int x, Stage& mine, const Stage& next, int buf) {
     fetch(x + NST < c_end ? x + NST : c_begin, mine, x + NST < c_end);
@@ -306,13 +312,11 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
     __syncthreads();
   };
   for (int x = c_begin - NST; x < c_end; x += NST) {
-    step(x, st0, st1, 0);
-    if (x + 1 >= c_end) break;
-    step(x + 1, st1, st2, 1);
-    if (x + 2 >= c_end) break;
-    step(x + 2, st2, st3, 0);
-    if (x + 3 >= c_end) break;
-    step(x + 3, st3, st0, 1);
+#pragma unroll
+    for (int k = 0; k < NST; ++k) {
+      step(x + k, st[k], st[(k + 1) % NST], k & 1);
+      if (x + k + 1 >= c_end) break;
+    }
   }
 
 #pragma unroll
