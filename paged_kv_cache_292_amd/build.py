@@ -26,6 +26,10 @@ HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: without this the decode
+    # kernel kept them in AGPRs and copied all of them to VGPRs and back on
+    # every loop iteration (and ran at 2 instead of 3 waves per SIMD)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-result",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]

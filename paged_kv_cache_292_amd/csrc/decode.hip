@@ -576,15 +576,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
 #pragma unroll
     for (int t = 0; t < EPL; ++t) {
+      // element t of rows 4c..4c+3 as bf16 pairs: one byte permute per word
+      // (bytes 0-1 of the first row's word, then of the second's; 2-3 for odd t)
       const int w = t >> 1;
-      uint32_t lo, hi;  // element t of rows 4c..4c+3, as bf16 pairs
-      if (t & 1) {
-        lo = (r.v[0][w] >> 16) | (r.v[1][w] & 0xFFFF0000u);
-        hi = (r.v[2][w] >> 16) | (r.v[3][w] & 0xFFFF0000u);
-      } else {
-        lo = (r.v[0][w] & 0xFFFFu) | (r.v[1][w] << 16);
-        hi = (r.v[2][w] & 0xFFFFu) | (r.v[3][w] << 16);
-      }
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel);
       const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pb, acc[t], 0, 0, 0);
     }
