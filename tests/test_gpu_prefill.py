@@ -158,3 +158,18 @@ def test_prefill_partitions_that_start_inside_a_chunk(case, part):
     ref = OA.paged_prefill(cs["q"], cs["ko"], cs["vo"], cs["tables"], cs["ctx"], cs["starts"],
                            scale, "bf16")
     assert_close(got, ref, "bf16", f"prefill case {case} p{part}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.07, 0.5])
+@pytest.mark.parametrize("part", [0, 64])
+def test_prefill_zero_negative_and_large_scale(scale, part):
+    """The kernel keeps the softmax reference in raw q.k units and folds a
+    negative scale into q: zero (every visible token weighs the same),
+    negative and large scales must still match the oracle."""
+    prior, chunks, Hq, Hkv, D, bs = CASES[0]
+    log(f"prefill scale={scale} partition={part}")
+    cs = _prefill_case(prior, chunks, Hq, Hkv, D, bs, seed=500)
+    got = _run(cs, Hq, D, part, scale)
+    ref = OA.paged_prefill(cs["q"], cs["ko"], cs["vo"], cs["tables"], cs["ctx"], cs["starts"],
+                           scale, "bf16")
+    assert_close(got, ref, "bf16", f"prefill scale {scale} p{part}")
