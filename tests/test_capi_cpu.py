@@ -341,3 +341,32 @@ def test_decode_rejects_too_many_partitions():
     st = _decode(part=16, max_ctx=16 * 70000, max_blocks=70000, q=1, k=1, v=1, tables=1, ctx=1,
                  out=1, ws=1, ws_bytes=1 << 62)
     assert st == -1 and "partitions" in P.lib.pkv_last_error().decode()
+
+
+def _decode_write(**kw):
+    # fake device addresses: every case below must fail validation before any launch
+    args = dict(out=0x100000, q=0x200000, nk=0x300000, nv=0x400000, ks=512, vs=512, k=0x500000,
+                v=0x600000, tables=0x700000, max_blocks=4, ctx=0x800000, max_ctx=64, B=2, Hq=4,
+                Hkv=4, D=128, bs=16, N=8, scale=0.1, part=0, ws=0, ws_bytes=0, dtype=P.BF16)
+    args.update(kw)
+    return P.lib.pkv_paged_attention_decode_write(
+        args["out"], args["q"], args["nk"], args["nv"], args["ks"], args["vs"], args["k"], args["v"],
+        args["tables"], args["max_blocks"], args["ctx"], None, args["max_ctx"], args["B"], args["Hq"],
+        args["Hkv"], args["D"], args["bs"], args["N"], args["scale"], args["part"], args["ws"],
+        args["ws_bytes"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nk=None), -1), (dict(nv=None), -1),                       # missing new rows
+    (dict(ks=511), -1), (dict(vs=100), -1),                         # stride below Hkv * D
+    (dict(ks=513), -1), (dict(vs=520, dtype=P.BF16), 0),            # 16-byte multiples
+    (dict(nk=0x300008), -1), (dict(k=0x500004), -1),                # misaligned pointers
+    (dict(D=96), -2), (dict(Hq=6, Hkv=4), -1), (dict(part=24), -1),  # the decode checks
+    (dict(out=None), -1), (dict(tables=None), -1),
+])
+def test_decode_write_rejects_bad_arguments_before_launch(kw, code):
+    if code == 0:  # a valid stride: make it fail later, on a missing output
+        kw = dict(kw, out=None)
+        code = -1
+    assert _decode_write(**kw) == code
+    assert P.lib.pkv_last_error().decode()
