@@ -225,6 +225,32 @@ def load_traffic(workload: str, path_name: str, kind: str):
 HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, per direction, published
 
 
+def read_ceiling(P, torch, buf, stream, achieved_gbs: float) -> dict:
+    """What HBM delivers to a plain read stream on this GPU: the library's
+    streaming-read kernel (the decode kernels' 16-byte non-temporal loads
+    and nothing else) over ``buf`` (the K cache, far larger than the
+    caches), best of a few grid sizes, 5 timed reads each after one warm-up;
+    and the decode kernel's rate as a fraction of it."""
+    cus = torch.cuda.get_device_properties(buf.device).multi_processor_count
+    nbytes = buf.numel() * buf.element_size()
+    best, best_wg = 0.0, 0
+    for mult in (1, 2, 4, 8, 16):
+        wg = cus * mult
+        out = torch.empty(wg, dtype=torch.int32, device=buf.device)
+        P.stream_read(buf, out, wg, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            P.stream_read(buf, out, wg, stream)
+        e1.record(stream)
+        e1.synchronize()
+        gbs = 5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if gbs > best:
+            best, best_wg = gbs, wg
+    return {"GBps": round(best, 1), "frac": round(achieved_gbs / best, 4), "bytes": int(nbytes),
+            "workgroups": best_wg, "kernel": "stream_read (16-byte non-temporal loads only)"}
+
+
 def run_swap(args) -> int:
     """Swap round trips of the shape's batch: every step, the host allocator
     swaps a quarter of the sequences out (every 4th, shared blocks once),
@@ -704,6 +730,10 @@ def main() -> int:
     tr = load_traffic(s.name, args.path, "prefill" if chunk else "decode")
     if tr is not None and tr["steps"] == args.steps and tr["warmup"] == args.warmup:
         res["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
+    # a pool at least twice the 256 MB last-level cache, so the reads stream from HBM
+    if not chunk and k_cache.numel() * k_cache.element_size() >= (512 << 20):
+        res["roofline"]["read_ceiling"] = read_ceiling(P, torch, k_cache, stream,
+                                                       res["roofline"]["achieved"])
     if args.calibrate_copy:
         # block i -> block N/2 + i for M blocks, K and V: M * block bytes read and
         # written per cache.  Done after timing; the cache contents are not used again.

@@ -154,6 +154,19 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t block_size, int32_t max_context_len,
                                   int32_t partition_size, pkv_dtype dtype);
 
+/* Streaming-read reference for the roofline (no step of the method): reads
+ * `bytes` of device memory at `src` once with 16-byte non-temporal loads,
+ * the loads the decode kernels stream K and V with, and no other work.  The
+ * rate it reaches on a buffer far larger than the caches is the read
+ * ceiling the decode kernels are compared with.  `out` (device, uint32
+ * [workgroups], caller-owned) receives one XOR of the 32-bit words each
+ * workgroup read; the XOR of all entries is the XOR of every word of the
+ * buffer.  `workgroups` (1 .. 2^20) sets the grid of 256-thread workgroups.
+ * src must be 16-byte aligned and bytes a multiple of 16; errors are
+ * reported before any launch.  Asynchronous on `stream`. */
+pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* out, int32_t workgroups,
+                           void* stream);
+
 /* Which decode kernel later calls use, process-wide (for tests and
  * benchmarks): PKV_PATH_AUTO (default) picks the matrix-core kernel for bf16
  * groups of 4..16 query heads and the vector kernel otherwise; PKV_PATH_VALU

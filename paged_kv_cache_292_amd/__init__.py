@@ -19,7 +19,7 @@ __all__ = [
     "LIB_PATH", "lib", "PkvError", "F32", "BF16", "PARTITION_AUTO",
     "kv_reshape_and_cache", "paged_attention_decode", "paged_attention_decode_write",
     "decode_workspace_bytes",
-    "decode_partition_size", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned", "longest_first_order",
+    "decode_partition_size", "stream_read", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned", "longest_first_order",
     "paged_attention_prefill", "prefill_workspace_bytes", "prefill_partition_size",
     "swap_blocks", "SWAP_OUT", "SWAP_IN",
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
@@ -49,6 +49,7 @@ EXPORTS = {
                                         _i64, _i64, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_stream_read": (_i32, [_vp, _sz, _vp, _i32, _vp]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                           _i32, _vp]),
@@ -179,6 +180,17 @@ def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
                           max_context_len, partition_size=PARTITION_AUTO, dtype=BF16) -> int:
     return int(lib.pkv_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                              block_size, max_context_len, partition_size, dtype))
+
+
+def stream_read(src, out, workgroups: int, stream=None) -> None:
+    """Read every byte of the device tensor ``src`` once (16-byte
+    non-temporal loads, nothing else): the streaming-read reference of the
+    decode roofline.  ``out`` is a device uint32/int32 tensor of at least
+    ``workgroups`` entries; entry w receives the XOR of the 32-bit words
+    workgroup w read."""
+    assert out.numel() >= workgroups
+    _check(lib.pkv_stream_read(src.data_ptr(), src.numel() * src.element_size(), out.data_ptr(),
+                               int(workgroups), _stream_ptr(stream)), "stream_read")
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,

@@ -263,6 +263,17 @@ def test_cache_write_rejects_bad_arguments(kw, code):
     assert st == code
 
 
+@pytest.mark.parametrize("src,nbytes,out,wg", [
+    (None, 1024, 0x1000, 4), (0x1000, 1024, None, 4),   # NULL pointers
+    (0x1008, 1024, 0x1000, 4), (0x1000, 1000, 0x1000, 4),  # misaligned source, ragged size
+    (0x1000, 1024, 0x1000, 0), (0x1000, 1024, 0x1000, (1 << 20) + 1),  # grid out of range
+])
+def test_stream_read_rejects_bad_arguments(src, nbytes, out, wg):
+    """Fake device addresses: every case fails validation before any launch."""
+    assert P.lib.pkv_stream_read(src, nbytes, out, wg, None) == -1
+    assert b"stream_read" in P.lib.pkv_last_error()
+
+
 def test_copy_blocks_rejects_bad_arguments():
     assert P.lib.pkv_copy_blocks(1, 1, 1, -1, 4, 16, 2, 64, P.BF16, None) == -1
     assert P.lib.pkv_copy_blocks(1, 1, 1, 0, 4, 16, 2, 64, P.BF16, None) == 0
