@@ -65,6 +65,11 @@ def test_full_shapes_sampled(cfg):
         got1 = run_decode(st, 0)
         assert_close(np.stack([got1[b, h] for b, h in pairs]), ref, s.dtype,
                      f"{s.name} full single pass")
+    if cfg == 4:  # and the shape's own 512-token partitions (up to 64 per sequence)
+        got5 = run_decode(st, 512)
+        assert np.isfinite(got5).all()
+        assert_close(np.stack([got5[b, h] for b, h in pairs]), ref, s.dtype,
+                     f"{s.name} full 512-token partitions")
 
 
 @pytest.fixture
