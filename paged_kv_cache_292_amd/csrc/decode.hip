@@ -701,6 +701,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the partitions of one (sequence, query head).
 // out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - max_p m_p).
+// Lane p computes partition p's weight (64 partitions at a time); the
+// weighted sum then walks the partitions with every lane on its own dims,
+// unrolled so that the loads of several partitions are in flight together
+// (one partition at a time left the kernel waiting on memory latency).
 template <typename T, int D>
 __global__ __launch_bounds__(64) void reduce_partitions_kernel(AttnArgs a) {
   constexpr int DPT = D / 64;
@@ -723,12 +727,32 @@ __global__ __launch_bounds__(64) void reduce_partitions_kernel(AttnArgs a) {
   float O[DPT];
 #pragma unroll
   for (int j = 0; j < DPT; ++j) O[j] = 0.0f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+  for (int p0 = 0; p0 < nparts; p0 += 64) {
+    const int p = p0 + t;
+    const float w = p < nparts ? ml[2 * p + 1] * fast_exp2(ml[2 * p] - M) : 0.0f;
     L += w;
+    const int cnt = min(64, nparts - p0);
+    const float* pg = po + size_t(p0) * D + t;
+    for (int q0 = 0; q0 < cnt; q0 += 8) {
+      // eight partitions' loads first (past the count: the last one again,
+      // with weight 0), then their products
+      float v[8][DPT];
 #pragma unroll
-    for (int j = 0; j < DPT; ++j) O[j] = fmaf(w, po[size_t(p) * D + j * 64 + t], O[j]);
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) v[r][j] = pg[size_t(min(q0 + r, cnt - 1)) * D + j * 64];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float wr = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(q0 + r, 63)));
+        const float wq = q0 + r < cnt ? wr : 0.0f;
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) O[j] = fmaf(wq, v[r][j], O[j]);
+      }
+    }
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
   const float inv = 1.0f / L;
 #pragma unroll
   for (int j = 0; j < DPT; ++j) store_elem<T>(a.out, head * D + j * 64 + t, O[j] * inv);
