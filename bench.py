@@ -730,8 +730,9 @@ def main() -> int:
     tr = load_traffic(s.name, args.path, "prefill" if chunk else "decode")
     if tr is not None and tr["steps"] == args.steps and tr["warmup"] == args.warmup:
         res["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
-    # a pool at least twice the 256 MB last-level cache, so the reads stream from HBM
-    if not chunk and k_cache.numel() * k_cache.element_size() >= (512 << 20):
+    # a pool at least 1.5 times the 256 MB last-level cache: a repeated pass
+    # over it evicts every line before its reuse, so the reads stream from HBM
+    if not chunk and k_cache.numel() * k_cache.element_size() >= (384 << 20):
         res["roofline"]["read_ceiling"] = read_ceiling(P, torch, k_cache, stream,
                                                        res["roofline"]["achieved"])
     if args.calibrate_copy:
