@@ -12,9 +12,17 @@
 // through LDS.
 #include "attn_common.h"
 
-// Register stages of the K/V prefetch (chunks in flight per workgroup; even).
+// Tokens of K/V staged in LDS per barrier by 8-wave workgroups (a multiple
+// of 32).  Measured on MI355X (16 sequences x 40 heads of 128, 512-token
+// chunks): 32 tokens 738 TFLOP/s, 64 tokens 761, 96 713, 128 722; two
+// 32-token passes of the products per barrier halve the barriers.
+#ifndef PKV_PREFILL_CHUNK
+#define PKV_PREFILL_CHUNK 64
+#endif
+// Register stages of the K/V prefetch (chunks in flight per workgroup; even;
+// 0 = 128 tokens in flight).
 #ifndef PKV_PREFILL_STAGES
-#define PKV_PREFILL_STAGES 4
+#define PKV_PREFILL_STAGES 0
 #endif
 
 namespace pkv {
@@ -27,12 +35,14 @@ namespace {
 // head, partition); a tile is 16 (query, head) rows, floor(16 / G)
 // consecutive queries times the G query heads of the kv head, the 16 operand
 // columns of the matrix products (the decode kernel's layout, with queries
-// added), and each wave owns TPW consecutive tiles.  Each 32-token K/V chunk
-// is loaded once by the whole workgroup — whole rows, streamed — into a
-// double-buffered LDS tile; every wave reads each K and V operand from LDS
-// once and uses it for all of its tiles (LDS reads per flop fall with TPW).
-// Both products are 32-deep matrix instructions: q.K^T over head_dim, and
-// P.V over the chunk's 32 tokens, its V operand read transposed from LDS.
+// added), and each wave owns TPW consecutive tiles.  Each K/V chunk (64
+// tokens for 8-wave workgroups, 32 for 4-wave ones) is loaded once by the
+// whole workgroup — whole rows, streamed — into a double-buffered LDS tile,
+// one barrier per chunk; every wave reads each K and V operand from LDS once
+// and uses it for all of its tiles (LDS reads per flop fall with TPW).  The
+// products run over the chunk in 32-token passes, both on 32-deep matrix
+// instructions: q.K^T over head_dim, and P.V over the pass's 32 tokens, its
+// V operand read transposed from LDS.
 // The next chunks' loads are in flight while the current one is computed.
 // Tiles that see no token of a chunk (the causal boundary) skip its math;
 // their waves keep to the barriers.
@@ -48,7 +58,11 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   // k/4; 8x as long unpadded) — and the chunk stores run at full write rate.
   constexpr int PITCH_K = D == 128 ? RB + 32 : RB + 16;
   constexpr int PITCH_V = PITCH_K;
-  constexpr int CH = 32;               // tokens per K/V chunk (one barrier each)
+  // tokens per K/V chunk (one barrier each): 4-wave workgroups keep 32, as
+  // their lanes would need twice the staging registers for longer chunks
+  constexpr int CH = NWP >= 8 ? PKV_PREFILL_CHUNK : 32;
+  constexpr int SUB = 32;              // tokens per pass of the products
+  static_assert(CH % SUB == 0, "a chunk is whole passes");
   constexpr int NBC = CH / BS;         // cache blocks per chunk
   static_assert(CH % BS == 0, "a chunk covers whole blocks");
   constexpr int LPR = RB / 16;         // 16-byte pieces per row
@@ -200,10 +214,12 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   };
 
   auto compute = [&](int ch, int buf) {
-    const int tc = ch * CH;
-    if (tc >= t1_max) return;  // none of this wave's tiles sees a token of this chunk
-    const char* ks = s_k[buf];
-    const char* vs = s_v[buf];
+#pragma unroll
+   for (int sb = 0; sb < CH / SUB; ++sb) {
+    const int tc = ch * CH + sb * SUB;
+    if (tc >= t1_max) break;  // none of this wave's tiles sees a token from here on
+    const char* ks = s_k[buf] + sb * SUB * PITCH_K;
+    const char* vs = s_v[buf] + sb * SUB * PITCH_V;
     // S^T = K . Q^T for every tile and each 16-token half h of the chunk,
     // each K operand read once
     f32x4_t s[TPW][2];
@@ -229,7 +245,7 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
       }
       // sc[4h + i]: token tc + 16h + 4c + i of query row n
       float sc[8];
-      if (tc >= t0 && tc + CH <= t1[u] && tc + CH - 1 <= pos_lo[u]) {  // every row sees every token
+      if (tc >= t0 && tc + SUB <= t1[u] && tc + SUB - 1 <= pos_lo[u]) {  // every row sees every token
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -286,22 +302,23 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
       for (int u = 0; u < TPW; ++u)
         acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u], acc[u][t], 0, 0, 0);
     }
+   }
   };
 
-  // Pipeline, prefetch distance 4: the global loads of chunk x + 4 are
-  // issued before chunk x is computed and reach LDS only after chunk x + 3 is
-  // computed, so four chunks are in flight per workgroup.  With one chunk in
-  // flight the loads, not the math, set the pace (measured: 2.3x slower than
-  // the same kernel without global loads): a workgroup needs tens of KB in
-  // flight to cover the memory latency (four 32-token chunks are 64 KB per
-  // workgroup at head_dim 128).  Four register stages rotate; two LDS
-  // buffers alternate by the chunk's parity; one barrier per chunk.  The loop
-  // starts four chunks early (those steps only fetch and store), so every
-  // fetch comes from the same loop body.
+  // Pipeline, prefetch distance NST (4 chunks of 32 tokens or 2 of 64: 128
+  // tokens either way): the global loads of chunk x + NST are issued before
+  // chunk x is computed and reach LDS only after chunk x + NST - 1 is
+  // computed.  With one 32-token chunk in flight the loads, not the math, set
+  // the pace (measured: 2.3x slower than the same kernel without global
+  // loads): a workgroup needs tens of KB in flight to cover the memory
+  // latency (128 tokens are 64 KB per workgroup at head_dim 128).  NST
+  // register stages rotate; two LDS buffers alternate by the chunk's parity;
+  // one barrier per chunk.  The loop starts NST chunks early (those steps
+  // only fetch and store), so every fetch comes from the same loop body.
   // the query operands (loaded above) are complete before the pipeline
   // starts, so no wait inside it has to cover them
   __builtin_amdgcn_s_waitcnt(0);
-  constexpr int NST = PKV_PREFILL_STAGES;
+  constexpr int NST = PKV_PREFILL_STAGES > 0 ? PKV_PREFILL_STAGES : (CH >= 64 ? 2 : 4);
   static_assert(NST % 2 == 0, "chunk x uses LDS buffer (x - c_begin) % 2 in every round");
   Stage st[NST];
   // step of chunk x (its register stage `mine`, the next chunk's `next`)
