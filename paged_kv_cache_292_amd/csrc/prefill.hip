@@ -392,21 +392,50 @@ __global__ __launch_bounds__(256) void merge_prefill_kernel(AttnArgs a) {
   const int nparts = (t_end + a.partition - 1) / a.partition;
   if (nparts <= 1) return;  // written directly by the partition kernel
   const int rows = (q_last - q_first + 1) * G;
-  for (int i = threadIdx.x; i < rows * D; i += 256) {
-    const int r = i / D;
-    const int d = i % D;
+  // One wave per valid row: lane p weighs partition p (64 at a time), then
+  // every lane sums its D/64 dims over the partitions, eight partitions'
+  // loads in flight per step (the decode merge's scheme).
+  constexpr int DPT = D / 64;
+  const int lane = threadIdx.x & 63;
+  for (int r = threadIdx.x >> 6; r < rows; r += 4) {
     const size_t row = (size_t(qrow0) + q_first + r / G) * Hq + size_t(kvh) * G + r % G;
     const float* ml = a.part_ml + 2 * row * a.max_parts;
     const float* po = a.part_o + row * a.max_parts * D;
     float M = -FLT_MAX;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-    float L = 0.0f, O = 0.0f;
-    for (int p = 0; p < nparts; ++p) {
-      const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+    for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.0f;
+    float O[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) O[j] = 0.0f;
+    for (int p0 = 0; p0 < nparts; p0 += 64) {
+      const int p = p0 + lane;
+      const float w = p < nparts ? ml[2 * p + 1] * fast_exp2(ml[2 * p] - M) : 0.0f;
       L += w;
-      O = fmaf(w, po[size_t(p) * D + d], O);
+      const int cnt = min(64, nparts - p0);
+      const float* pg = po + size_t(p0) * D + lane;
+      for (int q0 = 0; q0 < cnt; q0 += 8) {
+        float v[8][DPT];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int j = 0; j < DPT; ++j) v[k][j] = pg[size_t(min(q0 + k, cnt - 1)) * D + j * 64];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float wk = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(q0 + k, 63)));
+          const float wq = q0 + k < cnt ? wk : 0.0f;
+#pragma unroll
+          for (int j = 0; j < DPT; ++j) O[j] = fmaf(wq, v[k][j], O[j]);
+        }
+      }
     }
-    store_elem<uint16_t>(a.out, row * D + d, L > 0.0f ? O / L : 0.0f);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+#pragma unroll
+    for (int j = 0; j < DPT; ++j)
+      store_elem<uint16_t>(a.out, row * D + j * 64 + lane, L > 0.0f ? O[j] / L : 0.0f);
   }
 }
 // ---------------------------------------------------------------------------
