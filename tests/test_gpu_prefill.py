@@ -148,8 +148,9 @@ def test_prefill_tile_before_the_context_start_next_to_live_tiles():
 @pytest.mark.parametrize("part", [16, 48])
 def test_prefill_partitions_that_start_inside_a_chunk(case, part):
     """Partitions of 16 or 48 tokens (multiples of the block size, not of the
-    kernel's 32-token K/V chunk): every other partition starts in the middle
-    of a chunk, whose first half belongs to the previous partition."""
+    kernel's 32- or 64-token K/V chunks): partitions start in the middle of a
+    chunk, whose first part belongs to the previous partition (at 16 tokens
+    also exactly between the two 32-token passes of a 64-token chunk)."""
     prior, chunks, Hq, Hkv, D, bs = CASES[case]
     log(f"prefill case {case} partition={part} (starts inside a chunk)")
     cs = _prefill_case(prior, chunks, Hq, Hkv, D, bs, seed=400 + case)
@@ -163,9 +164,9 @@ def test_prefill_partitions_that_start_inside_a_chunk(case, part):
 @pytest.mark.parametrize("scale", [0.0, -0.07, 0.5])
 @pytest.mark.parametrize("part", [0, 64])
 def test_prefill_zero_negative_and_large_scale(scale, part):
-    """The kernel keeps the softmax reference in raw q.k units and folds a
-    negative scale into q: zero (every visible token weighs the same),
-    negative and large scales must still match the oracle."""
+    """The kernel scales the q.k products into base-2 logits before its
+    running maximum: zero (every visible token weighs the same), negative
+    (the order of the logits flips) and large scales must match the oracle."""
     prior, chunks, Hq, Hkv, D, bs = CASES[0]
     log(f"prefill scale={scale} partition={part}")
     cs = _prefill_case(prior, chunks, Hq, Hkv, D, bs, seed=500)
