@@ -619,12 +619,17 @@ def main() -> int:
         np.copyto(h_flat[j], host_flat)
         ds = i % 2
         d_slots, d_tables, d_ctx, d_order = d_views[ds]
-        if i >= 2:
+        # one stream orders everything by itself; with a side stream, the
+        # upload waits for the attention that last read its buffer and the
+        # attention for the upload
+        serial = up_stream is stream
+        if i >= 2 and not serial:
             up_stream.wait_event(att_done[ds])  # step i-2's attention read this buffer
         P.upload_pinned(d_stages[ds], h_stage[j], stream=up_stream)
         copied[j].record(up_stream)
-        up_done[ds].record(up_stream)
-        stream.wait_event(up_done[ds])
+        if not serial:
+            up_done[ds].record(up_stream)
+            stream.wait_event(up_done[ds])
         if step_tok and not fused_write:
             P.kv_reshape_and_cache(new_k_steps[i], new_v_steps[i], k_cache, v_cache, d_slots)
         if i in ev:
@@ -644,7 +649,8 @@ def main() -> int:
                                      seq_order=d_order if use_order else None)
         if i in ev:
             ev[i][1].record(stream)
-        att_done[ds].record(stream)
+        if not serial:
+            att_done[ds].record(stream)
         ctx_hist.append(cx)
         host_s.append(time.perf_counter() - t_h)
 
