@@ -736,6 +736,14 @@ def main() -> int:
     tr = load_traffic(s.name, args.path, "prefill" if chunk else "decode")
     if tr is not None and tr["steps"] == args.steps and tr["warmup"] == args.warmup:
         res["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
+    elif tr is not None:
+        # other step counts change the contexts the launches read: the
+        # counter run's traffic per algorithmic byte, applied to this run's
+        # algorithmic bytes per launch
+        res["roofline"]["traffic"] = int(round(tr["traffic_over_algorithmic"]
+                                               * res["roofline"]["algorithmic_bytes_per_launch"]))
+        res["roofline"]["traffic_scaled_from"] = (
+            f"{tr['steps']}-step counter run, traffic/algorithmic {tr['traffic_over_algorithmic']}")
     # a pool at least 1.5 times the 256 MB last-level cache: a repeated pass
     # over it evicts every line before its reuse, so the reads stream from HBM
     if not chunk and k_cache.numel() * k_cache.element_size() >= (384 << 20):
