@@ -676,6 +676,16 @@ def main() -> int:
     achieved = alg_per_launch / dec_avg_s / 1e9
     value = kv_t / elapsed / 1e9
 
+    # Unique K/V bytes of the last step (shared prefix blocks once): per
+    # distinct physical block, the most rows any sequence reads from it.
+    rows_of = {}
+    last_ctx = ctx_hist[-1].astype(np.int64)
+    for b in range(B):
+        nb = int((last_ctx[b] + bs - 1) // bs)
+        for k in range(nb):
+            blk = int(host_tb[b, k])
+            rows_of[blk] = max(rows_of.get(blk, 0), int(min(bs, last_ctx[b] - k * bs)))
+    unique_ratio = sum(rows_of.values()) / max(1, int(last_ctx.sum()))
     res = {
         "metric": "paged decode attention: effective KV HBM GB/s (% of peak), seq-tokens/s",
         "value": round(value, 2),
@@ -692,6 +702,8 @@ def main() -> int:
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(tok_t / elapsed, 1),
         "decode_tokens_per_s": round(B * K / elapsed, 1),
+        "kv_unique_over_logical": round(unique_ratio, 4),
+        "value_unique_GBps": round(value * unique_ratio, 2),
         "host_us_per_step": round(float(np.mean(host_s[timed])) * 1e6, 1),
         "host_wait_us_per_step": round(float(np.mean(wait_s[timed])) * 1e6, 1),
         "config": {
