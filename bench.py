@@ -720,6 +720,7 @@ def main() -> int:
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "avg_launch_us": round(dec_avg_s * 1e6, 2),
+            "median_launch_us": round(float(np.median(dec_ms)) * 1e3, 2),
             "algorithmic_bytes_per_launch": int(alg_per_launch),
             "event_timed_launches": len(timed_ev),
             # over every timed launch (the counters average all of them)
