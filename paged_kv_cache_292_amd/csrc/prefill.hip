@@ -215,94 +215,97 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
 
   auto compute = [&](int ch, int buf) {
 #pragma unroll
-   for (int sb = 0; sb < CH / SUB; ++sb) {
-    const int tc = ch * CH + sb * SUB;
-    if (tc >= t1_max) break;  // none of this wave's tiles sees a token from here on
-    const char* ks = s_k[buf] + sb * SUB * PITCH_K;
-    const char* vs = s_v[buf] + sb * SUB * PITCH_V;
-    // S^T = K . Q^T for every tile and each 16-token half h of the chunk,
-    // each K operand read once
-    f32x4_t s[TPW][2];
+    for (int sb = 0; sb < CH / SUB; ++sb) {
+      const int tc = ch * CH + sb * SUB;
+      if (tc >= t1_max) break;  // none of this wave's tiles sees a token from here on
+      const char* ks = s_k[buf] + sb * SUB * PITCH_K;
+      const char* vs = s_v[buf] + sb * SUB * PITCH_V;
+      // S^T = K . Q^T for every tile and each 16-token half h of the chunk,
+      // each K operand read once
+      f32x4_t s[TPW][2];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) s[u][0] = s[u][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int u = 0; u < TPW; ++u) s[u][0] = s[u][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < KSTEPS; ++j) {
-        const bf16x8_t kop = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(ks + (16 * h + n) * PITCH_K + 16 * c + 64 * j));
+        for (int j = 0; j < KSTEPS; ++j) {
+          const bf16x8_t kop = __builtin_bit_cast(
+              bf16x8_t,
+              *reinterpret_cast<const uint4*>(ks + (16 * h + n) * PITCH_K + 16 * c + 64 * j));
+#pragma unroll
+          for (int u = 0; u < TPW; ++u)
+            s[u][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                kop, __builtin_bit_cast(bf16x8_t, qop[u][j]), s[u][h], 0, 0, 0);
+        }
+      bf16x8_t pb[TPW];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        if (tc >= t1[u]) {  // wave-uniform: the tile adds nothing (every V row in LDS is finite)
+          pb[u] = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+          continue;
+        }
+        // sc[4h + i]: token tc + 16h + 4c + i of query row n
+        float sc[8];
+        // every row sees every token of the pass
+        if (tc >= t0 && tc + SUB <= t1[u] && tc + SUB - 1 <= pos_lo[u]) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[4 * h + i] = s[u][h][i] * a.scale_log2;
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = tc + 16 * h + 4 * c + i;
+              sc[4 * h + i] =
+                  (t >= t0 && t < t1[u] && t <= pos_n[u]) ? s[u][h][i] * a.scale_log2 : -INFINITY;
+            }
+        }
+        const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                               fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        if (__ballot(mx > m[u] + kLazyMax)) {
+          float hm = fmaxf(mx, __shfl_xor(mx, 16));
+          hm = fmaxf(hm, __shfl_xor(hm, 32));
+          const float mn = hm > m[u] + kLazyMax ? hm : m[u];
+          const float alpha = fast_exp2(m[u] - mn);
+          l[u] *= alpha;
+#pragma unroll
+          for (int t = 0; t < EPL; ++t) acc[u][t] *= alpha;
+          m[u] = mn;
+        }
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sc[i] - m[u]);
+        l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pb[u] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+      }
+      // O^T += V^T . P^T, tile by tile (one tile's V operand live at a time).
+      // The V^T operand of output tile t (dims 16t .. 16t+15) over the chunk's
+      // 32 tokens has k-slots 8c .. 8c+7 = tokens 4c .. 4c+3 and 16+4c ..
+      // 16+4c+3, the tokens whose scores lane (c, n) holds.  It comes straight
+      // from LDS with the transposing read: in each 16-lane group, lane k reads
+      // 8 bytes of row r0 + k/4 at dims 16t + 4(k%4), and lane j receives
+      // element j%4 of the reads of lanes j/4, j/4 + 4, + 8, + 12, i.e. dim
+      // 16t + j of rows r0 .. r0+3.
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s* lds_v4s;
+      const char* vrow = vs + (4 * c + (n >> 2)) * PITCH_V + 8 * (n & 3);
+#pragma unroll
+      for (int t = 0; t < EPL; ++t) {
+        const uint2 lo = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 32 * t)));
+        const uint2 hi = __builtin_bit_cast(
+            uint2,
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 16 * PITCH_V + 32 * t)));
+        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int u = 0; u < TPW; ++u)
-          s[u][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              kop, __builtin_bit_cast(bf16x8_t, qop[u][j]), s[u][h], 0, 0, 0);
+          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u], acc[u][t], 0, 0, 0);
       }
-    bf16x8_t pb[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      if (tc >= t1[u]) {  // wave-uniform: the tile adds nothing (every V row in LDS is finite)
-        pb[u] = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
-        continue;
-      }
-      // sc[4h + i]: token tc + 16h + 4c + i of query row n
-      float sc[8];
-      if (tc >= t0 && tc + SUB <= t1[u] && tc + SUB - 1 <= pos_lo[u]) {  // every row sees every token
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc[4 * h + i] = s[u][h][i] * a.scale_log2;
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = tc + 16 * h + 4 * c + i;
-            sc[4 * h + i] =
-                (t >= t0 && t < t1[u] && t <= pos_n[u]) ? s[u][h][i] * a.scale_log2 : -INFINITY;
-          }
-      }
-      const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      if (__ballot(mx > m[u] + kLazyMax)) {
-        float hm = fmaxf(mx, __shfl_xor(mx, 16));
-        hm = fmaxf(hm, __shfl_xor(hm, 32));
-        const float mn = hm > m[u] + kLazyMax ? hm : m[u];
-        const float alpha = fast_exp2(m[u] - mn);
-        l[u] *= alpha;
-#pragma unroll
-        for (int t = 0; t < EPL; ++t) acc[u][t] *= alpha;
-        m[u] = mn;
-      }
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sc[i] - m[u]);
-      l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      pb[u] = __builtin_bit_cast(
-          bf16x8_t, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
     }
-    // O^T += V^T . P^T, tile by tile (one tile's V operand live at a time).
-    // The V^T operand of output tile t (dims 16t .. 16t+15) over the chunk's
-    // 32 tokens has k-slots 8c .. 8c+7 = tokens 4c .. 4c+3 and 16+4c ..
-    // 16+4c+3, the tokens whose scores lane (c, n) holds.  It comes straight
-    // from LDS with the transposing read: in each 16-lane group, lane k reads
-    // 8 bytes of row r0 + k/4 at dims 16t + 4(k%4), and lane j receives
-    // element j%4 of the reads of lanes j/4, j/4 + 4, + 8, + 12, i.e. dim
-    // 16t + j of rows r0 .. r0+3.
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) v4s* lds_v4s;
-    const char* vrow = vs + (4 * c + (n >> 2)) * PITCH_V + 8 * (n & 3);
-#pragma unroll
-    for (int t = 0; t < EPL; ++t) {
-      const uint2 lo =
-          __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 32 * t)));
-      const uint2 hi = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 16 * PITCH_V + 32 * t)));
-      const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-      for (int u = 0; u < TPW; ++u)
-        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u], acc[u][t], 0, 0, 0);
-    }
-   }
   };
 
   // Pipeline, prefetch distance NST (4 chunks of 32 tokens or 2 of 64: 128
