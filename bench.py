@@ -739,7 +739,9 @@ def main() -> int:
             "kernel": "paged_attention_prefill (matrix-core partition kernel + merge)",
             "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "avg_launch_us": round(dec_avg_s * 1e6, 2), "flops_per_launch": int(fl),
+            "avg_launch_us": round(dec_avg_s * 1e6, 2),
+            "median_launch_us": round(float(np.median(dec_ms)) * 1e3, 2),
+            "flops_per_launch": int(fl),
             "event_timed_launches": len(timed_ev),
             "kv_GBps_unique": round(achieved, 1),
             "algorithmic_bytes_per_launch": int(alg_per_launch),
