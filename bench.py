@@ -736,7 +736,8 @@ def main() -> int:
         fl = float(np.mean([flops(ctx_hist[i]) for i in timed_ev]))  # the timed launches
         tflops = fl / dec_avg_s / 1e12
         res["roofline"] = {
-            "kernel": "paged_attention_prefill (matrix-core partition kernel + merge)",
+            "kernel": ("paged_attention_prefill (matrix-core kernel, single pass)" if part_used == 0
+                       else "paged_attention_prefill (matrix-core partition kernel + merge)"),
             "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
             "avg_launch_us": round(dec_avg_s * 1e6, 2),
