@@ -53,6 +53,10 @@ def _args():
     ap.add_argument("--staging-depth", type=int, default=8,
                     help="pinned staging buffers in flight (steps the host may run ahead)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode a batch with a shared prefix through "
+                         "paged_attention_decode_shared_prefix (the prefix partition computed "
+                         "once per tile of sharing sequences)")
     ap.add_argument("--prefix-cache", action="store_true",
                     help="measure admitting requests that share a cached 2,000-token system "
                          "prompt, against the same requests computed in full")
@@ -515,9 +519,19 @@ def main() -> int:
         d_qstart = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * chunk).to(dev)
         chunk_counts = np.full(B, chunk, dtype=np.int32)
     else:
+        if args.shared_prefix:
+            if not s.num_sharers or step_new:
+                raise SystemExit("--shared-prefix needs a batch with sharing and no new tokens")
+            args.partition = s.shared_prefix_tokens  # partition 0 is the shared prefix
         ws_bytes = P.decode_workspace_bytes(B, Hq, Hkv, D, bs, max_ctx_final, args.partition,
                                             dt_code)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    shared = bool(args.shared_prefix) and not chunk
+    if shared:
+        flag = np.zeros(B, dtype=np.int32)
+        flag[wl.sharers] = 1
+        d_members = torch.from_numpy(wl.sharers.astype(np.int32)).to(dev)
+        d_member_flag = torch.from_numpy(flag).to(dev)
     part_used = (P.prefill_partition_size(B, chunk, Hq, Hkv, max_ctx_final, args.partition)
                  if chunk else
                  P.decode_partition_size(B, Hq, Hkv, D, bs, max_ctx_final, args.partition, dt_code))
@@ -643,6 +657,11 @@ def main() -> int:
                                            v_cache, d_tables, d_ctx, maxc, s.scale,
                                            args.partition, workspace,
                                            seq_order=d_order if use_order else None)
+        elif shared:
+            P.paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, d_tables, d_ctx, maxc,
+                                                   s.scale, d_members, d_member_flag,
+                                                   s.shared_prefix_tokens, workspace,
+                                                   seq_order=d_order if use_order else None)
         else:
             P.paged_attention_decode(out, q, k_cache, v_cache, d_tables, d_ctx, maxc, s.scale,
                                      args.partition, workspace,
@@ -712,10 +731,13 @@ def main() -> int:
             "max_context": max_ctx_final, "new_tokens_per_step": B * step_tok,
             "partition_size": part_used, "kv_bytes_per_step": int(kv_t // K),
             "decode_path": args.path, "launch_order": args.order, "chunk_tokens": chunk,
+            "shared_prefix_decode": shared,
         },
         "roofline": {
             "kernel": ("paged_attention_decode" + ("_write (cache write fused)" if fused_write else "")
                        + (" (single pass)" if part_used == 0 else
+                          " (shared prefix once per tile of members, partition kernel + "
+                          "log-sum-exp merge)" if shared else
                           " (partition kernel + log-sum-exp merge)")),
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -749,7 +771,8 @@ def main() -> int:
             "algorithmic_bytes_all_timed_launches": int(np.mean(alg_bytes[timed])),
         }
         res["prefill_tokens_per_s"] = round(rows * K / elapsed, 1)
-    tr = load_traffic(s.name, args.path, "prefill" if chunk else "decode")
+    # (counters are recorded for the ordinary decode path only)
+    tr = None if shared else load_traffic(s.name, args.path, "prefill" if chunk else "decode")
     if tr is not None and tr["steps"] == args.steps and tr["warmup"] == args.warmup:
         res["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
     elif tr is not None:

@@ -193,6 +193,39 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q,
                                       size_t workspace_bytes, pkv_dtype dtype,
                                       void* stream);
 
+/* Paged decode for a batch in which some sequences share a prefix ("What Is
+ * vLLM …", section "How does PagedAttention work?", the memory-sharing
+ * step: sequences that share a prefix point at the same physical blocks).
+ * The result is that of pkv_paged_attention_decode with partition_size =
+ * prefix_tokens; partition 0 of every member, the shared prefix, is
+ * computed once for tiles of 16 / G members (G = num_q_heads /
+ * num_kv_heads): each K/V row of the prefix is read once per tile instead
+ * of once per member, and the tiles run in the same launch as the other
+ * partitions.
+ * members       device int32 [num_members]: the sharing sequences (distinct
+ *               indices into the batch).  Each member's first
+ *               prefix_tokens / block_size table entries must be the same
+ *               blocks, and its context must be longer than prefix_tokens;
+ *               otherwise its result is undefined (no access leaves the
+ *               tables, caches or workspace).
+ * member_flag   device int32 [num_seqs]: nonzero exactly for the members.
+ * prefix_tokens the shared length: a multiple of block_size and of 16, at
+ *               most max_context_len.
+ * workspace     at least pkv_decode_workspace_bytes(..., partition_size =
+ *               prefix_tokens, ...) bytes.
+ * Supported: bf16, grouped query heads on the matrix-core kernel (G 2..16);
+ * PKV_ERR_UNSUPPORTED otherwise.  Other arguments and errors as
+ * pkv_paged_attention_decode.
+ */
+pkv_status pkv_paged_attention_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    const int32_t* members, const int32_t* member_flag, int32_t num_members,
+    int32_t prefix_tokens, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+    void* stream);
+
 /* The decode step in one launch (the cache write fused into the attention):
  * for every sequence b with context_lens[b] > 0, its new token is its last
  * position p = context_lens[b] - 1 (already appended by the allocator), and

@@ -18,6 +18,7 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "lib", "PkvError", "F32", "BF16", "PARTITION_AUTO",
     "kv_reshape_and_cache", "paged_attention_decode", "paged_attention_decode_write",
+    "paged_attention_decode_shared_prefix",
     "decode_workspace_bytes",
     "decode_partition_size", "stream_read", "copy_blocks", "set_decode_path", "get_decode_path", "upload_pinned", "longest_first_order",
     "paged_attention_prefill", "prefill_workspace_bytes", "prefill_partition_size",
@@ -53,6 +54,10 @@ EXPORTS = {
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                           _i32, _vp]),
+    "pkv_paged_attention_decode_shared_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                                                        _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                        _f32, _vp, _vp, _i32, _i32, _vp, _sz,
+                                                        _i32, _vp]),
     "pkv_paged_attention_decode_write": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
                                                 _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
@@ -212,6 +217,29 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
         seq_order.data_ptr() if seq_order is not None else None, int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
         ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode")
+
+
+def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len: int, scale: float, members,
+                                         member_flag, prefix_tokens: int, workspace=None,
+                                         stream=None, seq_order=None) -> None:
+    """``paged_attention_decode`` with ``prefix_tokens``-token partitions, the
+    shared prefix of the sequences in ``members`` (device int32; their
+    tables start with the same blocks) computed once per tile of members.
+    ``member_flag``: device int32 [num_seqs], nonzero for the members;
+    ``workspace``: at least ``decode_workspace_bytes(..., prefix_tokens)``."""
+    N, bs, Hkv, D = k_cache.shape
+    B, Hq, _ = q.shape
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    M = members.numel() if members is not None else 0
+    _check(lib.pkv_paged_attention_decode_shared_prefix(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+        seq_order.data_ptr() if seq_order is not None else None, int(max_context_len), B, Hq,
+        Hkv, D, bs, N, float(scale), members.data_ptr() if M else None,
+        member_flag.data_ptr() if M else None, M, int(prefix_tokens), ws_ptr, ws_bytes,
+        _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode_shared_prefix")
 
 
 def paged_attention_decode_write(out, q, new_key, new_value, k_cache, v_cache, block_tables,

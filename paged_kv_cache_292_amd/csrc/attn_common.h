@@ -50,6 +50,14 @@ struct AttnArgs {
   int32_t num_blocks;
   int32_t partition;  // tokens per partition (multiple of 16), kSingle = one
   int32_t max_parts;
+  // Shared prefix (decode): grid rows z >= group_z0 compute partition 0 (the
+  // prefix) once for tiles of members whose tables start with the same
+  // blocks; member_flag[b] != 0 makes the sequence's own partition-0
+  // workgroup skip it.  members == nullptr: off.
+  const int32_t* members;
+  const int32_t* member_flag;
+  int32_t num_members;
+  int32_t group_z0;
   float scale_log2;   // scale * log2(e): logits are kept in base-2 units
 };
 

@@ -411,25 +411,41 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane >> 4;
   const int n = lane & 15;
-  const int part = blockIdx.x;
   const int kvh0 = blockIdx.y * HG;  // first kv head of the workgroup
   const int kvh = kvh0 + wave % HG;  // this wave's kv head
   const int stream = wave / HG;      // this wave's chunk stream
-  const int b = seq_of(a, blockIdx.z);
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
 
+  // Shared-prefix rows: a tile of 16 / G members sharing the prefix; its
+  // operand columns are (member, query head) pairs, and it computes the
+  // members' partition 0 (the prefix) with one read of the prefix's K/V.
+  const bool group = !WRITE && a.members != nullptr && int(blockIdx.z) >= a.group_z0;
+  const int mpg = 16 / G;  // members per tile
+  const int tile = group ? (int(blockIdx.z) - a.group_z0) * int(gridDim.x) + int(blockIdx.x) : 0;
+  const int tile_members = group ? min(mpg, a.num_members - tile * mpg) : 0;
+  if (group && tile_members <= 0) return;
+  auto member_seq = [&](int i) {
+    const int s = a.members[i];
+    return (unsigned)s < (unsigned)a.num_seqs ? s : 0;
+  };
+  const int part = group ? 0 : int(blockIdx.x);
+  const int b = group ? member_seq(tile * mpg) : seq_of(a, blockIdx.z);
+
   // The 16 operand columns are the G query heads of this kv head (padded
   // with zero columns); the query sees the sequence's whole context.
-  const int ctx = clamp_ctx(a, b);
+  const int ctx = group ? min(a.partition, a.ctx_cap) : clamp_ctx(a, b);
   const int t0 = part * a.partition;
   const int t1 = min(ctx, t0 + a.partition);
-  const int nparts = (ctx + a.partition - 1) / a.partition;
-  const int rows = G;  // valid operand columns
+  const int nparts = group ? 2 : (ctx + a.partition - 1) / a.partition;  // group: partials
+  if (!group && a.member_flag != nullptr && part == 0 && nparts >= 2 && a.member_flag[b] != 0)
+    return;  // the shared-prefix rows compute this partition
+  const int rows = group ? tile_members * G : G;  // valid operand columns
   const bool row_ok = n < rows;
   auto out_row_of = [&](int kv, int r) {  // (sequence, query head) index of column r
-    return size_t(b) * Hq + size_t(kv) * G + r;
+    return group ? size_t(member_seq(tile * mpg + r / G)) * Hq + size_t(kv) * G + r % G
+                 : size_t(b) * Hq + size_t(kv) * G + r;
   };
   auto out_row = [&](int r) { return out_row_of(kvh, r); };
   if (t0 >= t1) {
@@ -811,7 +827,13 @@ hipError_t launch_mfma(const AttnArgs& a, const NewRows& w, int num_seqs, hipStr
     hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kMfmaNW, kMfmaHG, WRITE>), grid,
                        dim3(kMfmaNW * 64), 0, st, a, w);
   } else {
-    const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
+    dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
+    if (!WRITE && a.members != nullptr && a.num_members > 0) {
+      // shared-prefix tiles after the sequences' rows, grid.x tiles per row
+      const int mpg = 16 / (a.num_q_heads / a.num_kv_heads);
+      const int tiles = (a.num_members + mpg - 1) / mpg;
+      grid.z += unsigned((tiles + int(grid.x) - 1) / int(grid.x));
+    }
     hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW, 1, WRITE>), grid, dim3(kNW * 64), 0, st, a,
                        w);
   }
@@ -939,7 +961,9 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, float scale,
                        int32_t partition_size, void* workspace, size_t workspace_bytes,
-                       pkv_dtype dtype, void* stream, const pkv::NewRows* w) {
+                       pkv_dtype dtype, void* stream, const pkv::NewRows* w,
+                       const int32_t* members = nullptr, const int32_t* member_flag = nullptr,
+                       int32_t num_members = 0) {
   if (dtype != PKV_F32 && dtype != PKV_BF16)
     return fail(PKV_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dtype));
   if (num_seqs < 0 || num_seqs > 65535)
@@ -988,6 +1012,10 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
   a.tables = block_tables;
   a.ctx_lens = context_lens;
   a.order = seq_order;
+  a.members = num_members > 0 ? members : nullptr;
+  a.member_flag = num_members > 0 ? member_flag : nullptr;
+  a.num_members = num_members;
+  a.group_z0 = num_seqs;
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.ctx_cap = cap;
@@ -1054,6 +1082,44 @@ extern "C" pkv_status pkv_paged_attention_decode(
                      max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                      partition_size, workspace, workspace_bytes, dtype, stream, nullptr);
+}
+
+extern "C" pkv_status pkv_paged_attention_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    const int32_t* members, const int32_t* member_flag, int32_t num_members,
+    int32_t prefix_tokens, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+    void* stream) {
+  const char* fn = "paged_attention_decode_shared_prefix";
+  if (dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      !pkv::use_mfma(true, num_q_heads / num_kv_heads) || pkv::kMfmaHG != 1)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "%s: needs the matrix-core kernel (grouped query heads, %d / %d)", fn,
+                num_q_heads, num_kv_heads);
+  if (num_members < 0 || num_members > num_seqs)
+    return fail(PKV_ERR_INVALID_ARG, "%s: num_members=%d outside [0, num_seqs=%d]", fn,
+                num_members, num_seqs);
+  if (num_members > 0 && (!members || !member_flag))
+    return fail(PKV_ERR_INVALID_ARG, "%s: NULL members or member_flag", fn);
+  const int32_t mpg = 16 / (num_q_heads / num_kv_heads);
+  if (int64_t(num_seqs) + (int64_t(num_members) + mpg - 1) / mpg > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "%s: %d sequences and %d members exceed the grid", fn,
+                num_seqs, num_members);
+  if (prefix_tokens <= 0 || block_size <= 0 || prefix_tokens % block_size != 0 ||
+      prefix_tokens % pkv::kChunk != 0 || prefix_tokens > max_context_len)
+    return fail(PKV_ERR_INVALID_ARG,
+                "%s: prefix_tokens=%d must be a positive multiple of block_size=%d and of %d, "
+                "at most max_context_len=%d", fn, prefix_tokens, block_size, pkv::kChunk,
+                max_context_len);
+  return decode_call(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, seq_order, max_context_len, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, prefix_tokens,
+                     workspace, workspace_bytes, dtype, stream, nullptr, members, member_flag,
+                     num_members);
 }
 
 extern "C" pkv_status pkv_paged_attention_decode_write(

@@ -1,0 +1,96 @@
+"""GPU parity of the shared-prefix decode: sequences whose tables start
+with the same blocks get their prefix partition computed once per tile of
+members (16 / G per tile), the rest as in the partitioned decode, merged by
+log-sum-exp.  Every case is checked against the fp64 oracle (which knows
+nothing of the sharing) and against the ordinary partitioned decode at the
+same partition length."""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_cases import assert_close, build_step, log, oracle_full, oracle_rows, run_decode
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+import paged_kv_cache_292_amd as P  # noqa: E402  (fails loudly when the library is missing)
+
+
+@pytest.fixture
+def decode_path():
+    """Select a decode kernel for one test, restore the automatic choice after."""
+    yield P.set_decode_path
+    P.set_decode_path(P.PATH_AUTO)
+
+
+def run_shared(st, members, prefix, order=None):
+    s = st.shape
+    out = torch.empty_like(st.q)
+    ws_bytes = P.decode_workspace_bytes(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                        s.block_size, st.max_ctx, prefix, P.BF16)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    flag = np.zeros(s.num_seqs, dtype=np.int32)
+    flag[np.asarray(members, dtype=np.int64)] = 1
+    m_dev = torch.from_numpy(np.ascontiguousarray(members, dtype=np.int32)).cuda()
+    f_dev = torch.from_numpy(flag).cuda()
+    so = torch.from_numpy(np.ascontiguousarray(order, dtype=np.int32)).cuda() if order is not None else None
+    P.paged_attention_decode_shared_prefix(out, st.q, st.k_cache, st.v_cache, st.tables_dev,
+                                           st.ctx_dev, st.max_ctx, s.scale, m_dev, f_dev,
+                                           prefix, ws, seq_order=so)
+    torch.cuda.synchronize()
+    from gpu_cases import OA, from_dev
+    return OA.widen(from_dev(out, s.dtype), s.dtype)
+
+
+def shape_with_sharing(B, hq, hkv, D, bs, prefix, sharers, lo, hi, seed):
+    return W.DecodeShape("shared", "bf16", B, hq, hkv, D, bs, "uniform", ctx_lo=lo, ctx_hi=hi,
+                         shared_prefix_tokens=prefix, num_sharers=sharers, seed=seed)
+
+
+@pytest.mark.parametrize("B,hq,hkv,D,bs,prefix,sharers", [
+    (16, 32, 8, 128, 32, 1024, 6),    # the GQA shape's structure, scaled
+    (12, 16, 2, 128, 16, 512, 9),     # G = 8: two members per tile, an odd count
+    (10, 32, 2, 128, 32, 256, 7),     # G = 16: one member per tile
+    (9, 6, 2, 64, 16, 96, 8),         # G = 3: five members per tile, head_dim 64
+    (8, 8, 4, 128, 16, 16, 8),        # G = 2 (matrix cores forced), one-block prefix, all share
+])
+def test_shared_prefix_matches_oracle(B, hq, hkv, D, bs, prefix, sharers, decode_path):
+    if hq // hkv < 4:
+        decode_path(P.PATH_MFMA)  # the automatic choice takes the vector kernel there
+    s = shape_with_sharing(B, hq, hkv, D, bs, prefix, sharers, prefix + 1, prefix + 900,
+                           seed=hq * 31 + prefix)
+    log(f"shared prefix B={B} G={hq // hkv} D={D} bs={bs} prefix={prefix} sharers={sharers}")
+    st = build_step(s, poison=True, pad=-5)
+    members = st.wl.sharers
+    ref = oracle_full(st)
+    got = run_shared(st, members, prefix)
+    assert_close(got, ref, "bf16", f"shared prefix G{hq // hkv} p{prefix}")
+    base = run_decode(st, prefix)
+    assert_close(got, base.astype(np.float64), "bf16", "shared prefix vs partitioned decode")
+    order = P.longest_first_order(st.ctx)
+    assert_close(run_shared(st, members, prefix, order), ref, "bf16", "shared prefix, ordered")
+
+
+def test_shared_prefix_with_no_members_is_the_partitioned_decode():
+    s = shape_with_sharing(6, 32, 8, 128, 32, 1024, 0, 200, 3000, seed=7)
+    st = build_step(s, poison=True)
+    got = run_shared(st, np.zeros(0, dtype=np.int64), 512)
+    np.testing.assert_array_equal(got, run_decode(st, 512))
+
+
+def test_shared_prefix_full_gqa_shape_sampled():
+    """The GQA decode batch at full size (256 sequences, 128 sharing a
+    1,024-token prefix): sampled rows of members and non-members."""
+    s = W.shape(3)
+    st = build_step(s, poison=True, pad=-1)
+    members = st.wl.sharers
+    got = run_shared(st, members, s.shared_prefix_tokens, P.longest_first_order(st.ctx))
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(3)
+    others = np.setdiff1d(np.arange(s.num_seqs), members)
+    bs_ = list(members[:4]) + list(rng.choice(members, 4)) + list(rng.choice(others, 4))
+    pairs = [(int(b), h) for b in bs_ for h in (0, 13, s.num_q_heads - 1)]
+    assert_close(np.stack([got[b, h] for b, h in pairs]), oracle_rows(st, pairs), "bf16",
+                 "full GQA shared prefix")
