@@ -588,7 +588,12 @@ def main() -> int:
         if fused_write:  # the new rows read from the input and written into the cache
             other += 2 * 2 * B * Hkv * D * E
         if part_used > 0:
-            np_ = (ctx + part_used - 1) // part_used
+            if shared:  # the prefix, then partitions of max(2048, prefix) tokens
+                F = s.shared_prefix_tokens
+                Pp = max(2048, F)
+                np_ = np.where(ctx > F, 1 + (ctx - F + Pp - 1) // Pp, 1)
+            else:
+                np_ = (ctx + part_used - 1) // part_used
             multi = np_[np_ > 1].sum()
             other += int(multi) * qrows * Hq * (D + 2) * 4 * 2
         return kv, kv + other

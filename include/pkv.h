@@ -196,12 +196,15 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q,
 /* Paged decode for a batch in which some sequences share a prefix ("What Is
  * vLLM …", section "How does PagedAttention work?", the memory-sharing
  * step: sequences that share a prefix point at the same physical blocks).
- * The result is that of pkv_paged_attention_decode with partition_size =
- * prefix_tokens; partition 0 of every member, the shared prefix, is
- * computed once for tiles of 16 / G members (G = num_q_heads /
- * num_kv_heads): each K/V row of the prefix is read once per tile instead
- * of once per member, and the tiles run in the same launch as the other
- * partitions.
+ * The result is that of pkv_paged_attention_decode (equal up to rounding):
+ * contexts are split into a first partition of prefix_tokens tokens and
+ * then partitions of max(2048, prefix_tokens) tokens, merged by
+ * log-sum-exp.  Partition 0 of every member, the shared prefix, is computed
+ * once for tiles of 16 / G members (G = num_q_heads / num_kv_heads): each
+ * K/V row of the prefix is read once per tile instead of once per member,
+ * and the tiles run in the same launch as the other partitions.  With
+ * num_members = 0 the call is pkv_paged_attention_decode with
+ * partition_size = prefix_tokens.
  * members       device int32 [num_members]: the sharing sequences (distinct
  *               indices into the batch).  Each member's first
  *               prefix_tokens / block_size table entries must be the same

@@ -58,6 +58,7 @@ struct AttnArgs {
   const int32_t* member_flag;
   int32_t num_members;
   int32_t group_z0;
+  int32_t first_part;  // > 0: partition 0 is this many tokens, the rest `partition` each
   float scale_log2;   // scale * log2(e): logits are kept in base-2 units
 };
 
@@ -79,6 +80,21 @@ __device__ __forceinline__ void query_range(const AttnArgs& a, int b, int& first
   hi = hi < lo ? lo : (hi > a.total_queries ? a.total_queries : hi);
   first = lo;
   count = hi - lo;
+}
+
+// Token range [start, start + length) of partition p and the number of
+// partitions of a ctx-token context (uniform unless first_part > 0).
+__device__ __forceinline__ int part_begin(const AttnArgs& a, int p) {
+  return a.first_part > 0 ? (p == 0 ? 0 : a.first_part + (p - 1) * a.partition)
+                          : p * a.partition;
+}
+__device__ __forceinline__ int part_length(const AttnArgs& a, int p) {
+  return a.first_part > 0 && p == 0 ? a.first_part : a.partition;
+}
+__device__ __forceinline__ int part_count(const AttnArgs& a, int ctx) {
+  if (a.first_part > 0)
+    return ctx <= a.first_part ? 1 : 1 + (ctx - a.first_part + a.partition - 1) / a.partition;
+  return (ctx + a.partition - 1) / a.partition;
 }
 
 __device__ __forceinline__ int clamp_ctx(const AttnArgs& a, int b) {

@@ -435,10 +435,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
 
   // The 16 operand columns are the G query heads of this kv head (padded
   // with zero columns); the query sees the sequence's whole context.
-  const int ctx = group ? min(a.partition, a.ctx_cap) : clamp_ctx(a, b);
-  const int t0 = part * a.partition;
-  const int t1 = min(ctx, t0 + a.partition);
-  const int nparts = group ? 2 : (ctx + a.partition - 1) / a.partition;  // group: partials
+  const int ctx = group ? min(part_length(a, 0), a.ctx_cap) : clamp_ctx(a, b);
+  const int t0 = part_begin(a, part);
+  const int t1 = min(ctx, t0 + part_length(a, part));
+  const int nparts = group ? 2 : part_count(a, ctx);  // group: partials
   if (!group && a.member_flag != nullptr && part == 0 && nparts >= 2 && a.member_flag[b] != 0)
     return;  // the shared-prefix rows compute this partition
   const int rows = group ? tile_members * G : G;  // valid operand columns
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(64) void reduce_partitions_kernel(AttnArgs a) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int ctx = clamp_ctx(a, b);
-  const int nparts = (ctx + a.partition - 1) / a.partition;
+  const int nparts = part_count(a, ctx);
   if (nparts <= 1) return;  // written directly by the partition kernel
   const size_t head = size_t(b) * a.num_q_heads + h;
   const float* ml = a.part_ml + 2 * head * a.max_parts;
@@ -865,6 +865,15 @@ bool wide_layout(bool bf16, int G, int num_kv_heads) {
 // batch, lengths up to 4096, and equal to partitioned over lengths 2k..8k;
 // with one 32k sequence among 127 short ones, 4096-token partitions give 6.5
 // TB/s where single pass gives 2.3).  Other kernels: resolve_partition.
+// Shared-prefix decode: the partitions after the prefix are the automatic
+// length (2048 tokens) or the prefix's, whichever is longer, so there are
+// never more partitions than with prefix-length partitions throughout (the
+// workspace size the call documents).
+int32_t shared_partition(int32_t max_context_len, int32_t prefix_tokens) {
+  (void)max_context_len;
+  return std::max<int32_t>(PKV_AUTO_PARTITION, prefix_tokens);
+}
+
 int32_t decode_partition(bool bf16, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t max_context_len, int32_t partition_size) {
   if (partition_size == PKV_PARTITION_AUTO && num_kv_heads > 0 &&
@@ -1000,10 +1009,20 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL pointer argument", fn);
 
-  const int32_t partition = pkv::decode_partition(dtype == PKV_BF16, num_q_heads, num_kv_heads,
-                                                  max_context_len, partition_size);
+  // Shared prefix: partition 0 is the prefix (first_part tokens), the rest
+  // partitions of the shared-prefix length rule (at least the prefix).
+  const int32_t first_part = num_members > 0 ? partition_size : 0;
+  const int32_t partition =
+      first_part > 0 ? pkv::shared_partition(max_context_len, first_part)
+                     : pkv::decode_partition(dtype == PKV_BF16, num_q_heads, num_kv_heads,
+                                             max_context_len, partition_size);
   const int32_t cap = int32_t(std::min<int64_t>(max_context_len,
                                                 int64_t(max_blocks_per_seq) * block_size));
+  // partitions of a context of n tokens
+  auto parts_of = [&](int64_t n) -> int64_t {
+    if (first_part > 0) return n <= first_part ? 1 : 1 + (n - first_part + partition - 1) / partition;
+    return (n + partition - 1) / partition;
+  };
   pkv::AttnArgs a{};
   a.out = out;
   a.q = q;
@@ -1023,10 +1042,14 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
   a.num_kv_heads = num_kv_heads;
   a.num_blocks = num_blocks;
   a.scale_log2 = scale * pkv::kLog2e;
+  a.first_part = first_part;
   int grid_parts = 1;
   if (partition > 0) {
-    const size_t need = pkv::workspace_for(num_seqs, num_q_heads, head_dim, max_context_len,
-                                           partition);
+    const size_t need =
+        first_part > 0 ? size_t(num_seqs) * num_q_heads * size_t(parts_of(max_context_len)) *
+                             (size_t(head_dim) + 2) * sizeof(float)
+                       : pkv::workspace_for(num_seqs, num_q_heads, head_dim, max_context_len,
+                                            partition);
     if (need > 0 && (!workspace || workspace_bytes < need))
       return fail(PKV_ERR_WORKSPACE,
                   "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -1034,12 +1057,12 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
     a.partition = partition;
     // the workspace is sized from max_context_len; partitions past the clamped
     // context are never launched
-    a.max_parts = int32_t((int64_t(max_context_len) + partition - 1) / partition);
+    a.max_parts = int32_t(parts_of(max_context_len));
     if (a.max_parts < 1) a.max_parts = 1;
     float* ws = static_cast<float*>(workspace);
     a.part_o = ws;
     a.part_ml = ws + size_t(num_seqs) * num_q_heads * a.max_parts * head_dim;
-    grid_parts = int((int64_t(cap) + partition - 1) / partition);
+    grid_parts = int(parts_of(cap));
     if (grid_parts < 1) grid_parts = 1;
     if (grid_parts > 65535)
       return fail(PKV_ERR_INVALID_ARG,
