@@ -147,6 +147,22 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _index_ptr(t, n: int, what: str, where: str, rows: bool = False):
+    """Device pointer of an index array the kernels read up to entry (or,
+    for ``rows``, row) ``n - 1``: a contiguous int32 device tensor.  A host
+    tensor, another dtype or too few entries would reach the kernel as a
+    bad address, so they are refused here.  ``None`` stays ``None``."""
+    import torch
+    if t is None:
+        return None
+    have = (t.shape[0] if t.dim() == 2 else -1) if rows else t.numel()
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or have < n:
+        raise ValueError(f"{where}: {what} must be a contiguous int32 device tensor with at least "
+                         f"{n} {'rows' if rows else 'entries'} (got {t.dtype}, {t.device}, "
+                         f"shape {tuple(t.shape)})")
+    return t.data_ptr()
+
+
 def _stream_ptr(stream) -> int:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -208,26 +224,30 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     ``decode_workspace_bytes(...)`` bytes when partitions are used;
     ``seq_order`` an optional device int32 launch order (longest first is
     fastest, see ``longest_first_order``)."""
+    fn = "paged_attention_decode"
     N, bs, Hkv, D = k_cache.shape
     B, Hq, _ = q.shape
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pkv_paged_attention_decode(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
-        seq_order.data_ptr() if seq_order is not None else None, int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
-        ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode")
+        _index_ptr(block_tables, B, "block_tables", fn, rows=True), block_tables.shape[1],
+        _index_ptr(context_lens, B, "context_lens", fn), _index_ptr(seq_order, B, "seq_order", fn),
+        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
+        ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), fn)
 
 
 def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens,
                                          max_context_len: int, scale: float, members,
                                          member_flag, prefix_tokens: int, workspace=None,
                                          stream=None, seq_order=None) -> None:
-    """``paged_attention_decode`` with ``prefix_tokens``-token partitions, the
-    shared prefix of the sequences in ``members`` (device int32; their
-    tables start with the same blocks) computed once per tile of members.
+    """``paged_attention_decode`` with a first partition of ``prefix_tokens``
+    tokens (then partitions of max(2048, prefix_tokens)): the shared prefix
+    of the sequences in ``members`` (device int32; their tables start with
+    the same blocks) is computed once per tile of members.
     ``member_flag``: device int32 [num_seqs], nonzero for the members;
     ``workspace``: at least ``decode_workspace_bytes(..., prefix_tokens)``."""
+    fn = "paged_attention_decode_shared_prefix"
     N, bs, Hkv, D = k_cache.shape
     B, Hq, _ = q.shape
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -235,11 +255,12 @@ def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
     M = members.numel() if members is not None else 0
     _check(lib.pkv_paged_attention_decode_shared_prefix(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
-        seq_order.data_ptr() if seq_order is not None else None, int(max_context_len), B, Hq,
-        Hkv, D, bs, N, float(scale), members.data_ptr() if M else None,
-        member_flag.data_ptr() if M else None, M, int(prefix_tokens), ws_ptr, ws_bytes,
-        _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode_shared_prefix")
+        _index_ptr(block_tables, B, "block_tables", fn, rows=True), block_tables.shape[1],
+        _index_ptr(context_lens, B, "context_lens", fn), _index_ptr(seq_order, B, "seq_order", fn),
+        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale),
+        _index_ptr(members, M, "members", fn) if M else None,
+        _index_ptr(member_flag, B, "member_flag", fn) if M else None, M, int(prefix_tokens), ws_ptr,
+        ws_bytes, _dtype_code(q), _stream_ptr(stream)), fn)
 
 
 def paged_attention_decode_write(out, q, new_key, new_value, k_cache, v_cache, block_tables,
@@ -256,15 +277,17 @@ def paged_attention_decode_write(out, q, new_key, new_value, k_cache, v_cache, b
         if tuple(t.shape) != (B, Hkv, D) or t.stride(2) != 1 or (Hkv > 1 and t.stride(1) != D):
             raise ValueError(f"paged_attention_decode_write: {nm} must be [{B}, {Hkv}, {D}] "
                              "with each sequence's row contiguous")
+    fn = "paged_attention_decode_write"
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pkv_paged_attention_decode_write(
         out.data_ptr(), q.data_ptr(), new_key.data_ptr(), new_value.data_ptr(),
         new_key.stride(0) if B else Hkv * D, new_value.stride(0) if B else Hkv * D,
-        k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
-        context_lens.data_ptr(), seq_order.data_ptr() if seq_order is not None else None,
+        k_cache.data_ptr(), v_cache.data_ptr(),
+        _index_ptr(block_tables, B, "block_tables", fn, rows=True), block_tables.shape[1],
+        _index_ptr(context_lens, B, "context_lens", fn), _index_ptr(seq_order, B, "seq_order", fn),
         int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size), ws_ptr,
-        ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_decode_write")
+        ws_bytes, _dtype_code(q), _stream_ptr(stream)), fn)
 
 
 def upload_pinned(dst, src_pinned, stream=None) -> None:
@@ -306,17 +329,19 @@ def paged_attention_prefill(out, q, query_start, max_queries_per_seq: int, k_cac
     """Chunked prefill: query rows ``query_start[b] .. query_start[b+1]-1`` of
     ``q [T, Hq, D]`` are the last tokens of sequence ``b`` and attend causally
     to its paged context.  ``query_start``: device int32 ``[B + 1]``."""
+    fn = "paged_attention_prefill"
     N, bs, Hkv, D = k_cache.shape
     T, Hq, _ = q.shape
     B = context_lens.shape[0]
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pkv_paged_attention_prefill(
-        out.data_ptr(), q.data_ptr(), query_start.data_ptr(), T, int(max_queries_per_seq),
-        k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
-        context_lens.data_ptr(), seq_order.data_ptr() if seq_order is not None else None,
+        out.data_ptr(), q.data_ptr(), _index_ptr(query_start, B + 1, "query_start", fn), T,
+        int(max_queries_per_seq), k_cache.data_ptr(), v_cache.data_ptr(),
+        _index_ptr(block_tables, B, "block_tables", fn, rows=True), block_tables.shape[1],
+        _index_ptr(context_lens, B, "context_lens", fn), _index_ptr(seq_order, B, "seq_order", fn),
         int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size), ws_ptr,
-        ws_bytes, _dtype_code(q), _stream_ptr(stream)), "paged_attention_prefill")
+        ws_bytes, _dtype_code(q), _stream_ptr(stream)), fn)
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:

@@ -381,3 +381,37 @@ def test_decode_write_rejects_bad_arguments_before_launch(kw, code):
         code = -1
     assert _decode_write(**kw) == code
     assert P.lib.pkv_last_error().decode()
+
+
+def test_wrappers_refuse_index_arrays_that_are_not_int32_device_tensors():
+    """Block tables, lengths, launch orders, query starts and member lists
+    reach the kernels as raw addresses; the binding refuses host tensors,
+    other dtypes and too few entries before any library call."""
+    import torch
+    import paged_kv_cache_292_amd as P
+
+    B, Hq, Hkv, D, bs, N = 2, 4, 2, 64, 16, 4
+    q = torch.zeros(B, Hq, D)
+    out = torch.zeros_like(q)
+    kc = torch.zeros(N, bs, Hkv, D)
+    tables = torch.zeros(B, 2, dtype=torch.int32)
+    ctx = torch.ones(B, dtype=torch.int32)
+    with pytest.raises(ValueError, match="paged_attention_decode: block_tables"):
+        P.paged_attention_decode(out, q, kc, kc, tables, ctx, 1, 0.1, 0)
+    with pytest.raises(ValueError, match="paged_attention_decode_write: block_tables"):
+        P.paged_attention_decode_write(out, q, torch.zeros(B, Hkv, D), torch.zeros(B, Hkv, D),
+                                       kc, kc, tables, ctx, 1, 0.1, 0)
+    with pytest.raises(ValueError, match="shared_prefix: block_tables"):
+        P.paged_attention_decode_shared_prefix(out, q, kc, kc, tables, ctx, 16, 0.1,
+                                               torch.zeros(1, dtype=torch.int32), ctx, 16)
+    with pytest.raises(ValueError, match="paged_attention_prefill: query_start"):
+        P.paged_attention_prefill(out, q, torch.tensor([0, 1, 2], dtype=torch.int32), 1, kc, kc,
+                                  tables, ctx, 1, 0.1, 0)
+    # each condition on its own
+    assert P._index_ptr(None, 5, "seq_order", "f") is None
+    for bad in (torch.zeros(B, dtype=torch.int64), torch.zeros(B, dtype=torch.int32),
+                torch.zeros(4, dtype=torch.int32)[::2]):
+        with pytest.raises(ValueError, match="f: context_lens must be a contiguous int32 device"):
+            P._index_ptr(bad, B, "context_lens", "f")
+    with pytest.raises(ValueError, match="at least 3 rows"):
+        P._index_ptr(tables, 3, "block_tables", "f", rows=True)
