@@ -147,19 +147,24 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _index_ptr(t, n: int, what: str, where: str, rows: bool = False):
+def _index_ptr(t, n: int, what: str, where: str, rows: bool = False, wide: bool = False,
+               cols: Optional[int] = None):
     """Device pointer of an index array the kernels read up to entry (or,
-    for ``rows``, row) ``n - 1``: a contiguous int32 device tensor.  A host
-    tensor, another dtype or too few entries would reach the kernel as a
-    bad address, so they are refused here.  ``None`` stays ``None``."""
+    for ``rows``, row) ``n - 1``: a contiguous int32 (``wide``: int64) device
+    tensor, with ``cols`` columns when given.  A host tensor, another dtype
+    or too few entries would reach the kernel as a bad address, so they are
+    refused here.  ``None`` stays ``None``."""
     import torch
     if t is None:
         return None
+    want = torch.int64 if wide else torch.int32
     have = (t.shape[0] if t.dim() == 2 else -1) if rows else t.numel()
-    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or have < n:
-        raise ValueError(f"{where}: {what} must be a contiguous int32 device tensor with at least "
-                         f"{n} {'rows' if rows else 'entries'} (got {t.dtype}, {t.device}, "
-                         f"shape {tuple(t.shape)})")
+    if (t.dtype != want or not t.is_cuda or not t.is_contiguous() or have < n
+            or (cols is not None and (t.dim() != 2 or t.shape[1] != cols))):
+        shape = f"[>= {n}, {cols}]" if cols is not None else f"at least {n} " + (
+            "rows" if rows else "entries")
+        raise ValueError(f"{where}: {what} must be a contiguous {str(want)[6:]} device tensor, "
+                         f"{shape} (got {t.dtype}, {t.device}, shape {tuple(t.shape)})")
     return t.data_ptr()
 
 
@@ -175,7 +180,8 @@ def kv_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None
     T = key.shape[0]
     _check(lib.pkv_kv_reshape_and_cache(
         key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        slot_mapping.data_ptr(), T, Hkv, D, bs, N,
+        _index_ptr(slot_mapping, T, "slot_mapping", "kv_reshape_and_cache", wide=True),
+        T, Hkv, D, bs, N,
         key.stride(0) if T else Hkv * D, value.stride(0) if T else Hkv * D,
         _dtype_code(k_cache), _stream_ptr(stream)), "kv_reshape_and_cache")
 
@@ -347,7 +353,8 @@ def paged_attention_prefill(out, q, query_start, max_queries_per_seq: int, k_cac
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     """``cache[dst] = cache[src]`` for each row ``(src, dst)`` of int64 ``pairs [P, 2]``."""
     N, bs, Hkv, D = k_cache.shape
-    _check(lib.pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(),
+    _check(lib.pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(),
+                               _index_ptr(pairs, 0, "pairs", "copy_blocks", wide=True, cols=2),
                                pairs.shape[0], N, bs, Hkv, D, _dtype_code(k_cache),
                                _stream_ptr(stream)), "copy_blocks")
 
@@ -364,7 +371,9 @@ def swap_blocks(k_cache, v_cache, k_host, v_host, pairs, direction: int, stream=
     if k_host.dtype != k_cache.dtype or v_host.dtype != k_cache.dtype:
         raise TypeError("host pools must have the cache dtype")
     _check(lib.pkv_swap_blocks(k_cache.data_ptr(), v_cache.data_ptr(), k_host.data_ptr(),
-                               v_host.data_ptr(), pairs.data_ptr(), pairs.shape[0], N, Nh, bs,
+                               v_host.data_ptr(),
+                               _index_ptr(pairs, 0, "pairs", "swap_blocks", wide=True, cols=2),
+                               pairs.shape[0], N, Nh, bs,
                                Hkv, D, _dtype_code(k_cache), int(direction), _stream_ptr(stream)),
            "swap_blocks")
 

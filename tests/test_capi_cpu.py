@@ -415,3 +415,15 @@ def test_wrappers_refuse_index_arrays_that_are_not_int32_device_tensors():
             P._index_ptr(bad, B, "context_lens", "f")
     with pytest.raises(ValueError, match="at least 3 rows"):
         P._index_ptr(tables, 3, "block_tables", "f", rows=True)
+    # int64 arrays: cache-write slots, block copy and swap pairs
+    with pytest.raises(ValueError, match="kv_reshape_and_cache: slot_mapping must be a contiguous "
+                                         "int64 device tensor"):
+        P.kv_reshape_and_cache(torch.zeros(B, Hkv, D), torch.zeros(B, Hkv, D), kc, kc,
+                               torch.zeros(B, dtype=torch.int64))
+    with pytest.raises(ValueError, match=r"copy_blocks: pairs .*\[>= 0, 2\]"):
+        P.copy_blocks(kc, kc, torch.zeros(1, 2, dtype=torch.int64))
+    with pytest.raises(ValueError, match="swap_blocks: pairs"):
+        P.swap_blocks(kc, kc, kc.clone(), kc.clone(), torch.zeros(1, 2, dtype=torch.int64),
+                      P.SWAP_OUT)
+    with pytest.raises(ValueError, match="int64"):
+        P._index_ptr(torch.zeros(3, 2, dtype=torch.int32), 0, "pairs", "f", wide=True, cols=2)
