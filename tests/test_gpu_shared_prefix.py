@@ -1,9 +1,10 @@
 """GPU parity of the shared-prefix decode: sequences whose tables start
 with the same blocks get their prefix partition computed once per tile of
 members (16 / G per tile), the rest as in the partitioned decode, merged by
-log-sum-exp.  Every case is checked against the fp64 oracle (which knows
-nothing of the sharing) and against the ordinary partitioned decode at the
-same partition length."""
+log-sum-exp.  The prefix is partition 0; later partitions are max(2048,
+prefix) tokens.  Every case is checked against the fp64 oracle (which knows
+nothing of the sharing) and against the ordinary partitioned decode with
+prefix-length partitions (equal up to rounding)."""
 import numpy as np
 import pytest
 
@@ -71,6 +72,24 @@ def test_shared_prefix_matches_oracle(B, hq, hkv, D, bs, prefix, sharers, decode
     assert_close(got, base.astype(np.float64), "bf16", "shared prefix vs partitioned decode")
     order = P.longest_first_order(st.ctx)
     assert_close(run_shared(st, members, prefix, order), ref, "bf16", "shared prefix, ordered")
+
+
+@pytest.mark.parametrize("prefix,lo,hi,bs", [
+    (256, 2500, 7000, 16),    # later partitions of 2048 tokens, up to four of them
+    (2560, 2561, 9000, 32),   # prefix over 2048: later partitions of the prefix's length
+])
+def test_shared_prefix_with_several_later_partitions(prefix, lo, hi, bs):
+    """Contexts that run several partitions past the prefix: the partition
+    boundaries after the prefix partition fall every max(2048, prefix) tokens
+    from its end, and every partition's partials meet in the merge."""
+    s = shape_with_sharing(6, 32, 8, 128, bs, prefix, 4, lo, hi, seed=prefix + lo)
+    log(f"shared prefix, later partitions: prefix={prefix} contexts {lo}..{hi} bs={bs}")
+    st = build_step(s, poison=True, pad=-3)
+    members = st.wl.sharers
+    ref = oracle_full(st)
+    got = run_shared(st, members, prefix, P.longest_first_order(st.ctx))
+    assert_close(got, ref, "bf16", f"shared prefix {prefix}, long contexts")
+    assert_close(run_shared(st, members, prefix), ref, "bf16", "unordered")
 
 
 def test_shared_prefix_with_no_members_is_the_partitioned_decode():
