@@ -168,6 +168,72 @@ def _index_ptr(t, n: int, what: str, where: str, rows: bool = False, wide: bool 
     return t.data_ptr()
 
 
+def _dense_ptr(t, shape, dtype, what: str, where: str, rows: bool = False):
+    """Device pointer of a dense operand the kernels read or write in full:
+    a tensor of element type ``dtype`` (the cache's) and exactly ``shape``,
+    contiguous (``rows``: only each row of the last two dimensions, as a
+    strided batch of ``[Hkv, D]`` rows), on the device.  Another element type
+    or shape would make a kernel read or write past the end of the buffer,
+    and a host tensor would reach it as a bad address, so all are refused
+    here.  Checked in that order, so each condition has its own message."""
+    if t.dtype != dtype:
+        raise ValueError(f"{where}: {what} must have the cache's element type {dtype} "
+                         f"(got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: {what} must have shape {list(shape)} (got {list(t.shape)})")
+    if rows:
+        dense = t.stride(-1) == 1 and (t.shape[-2] <= 1 or t.stride(-2) == t.shape[-1])
+    else:
+        dense = t.is_contiguous()
+    if not dense:
+        raise ValueError(f"{where}: {what} must be " + (
+            "row-contiguous (stride(-1) == 1, stride(-2) == head_dim)" if rows else "contiguous"))
+    if not t.is_cuda:
+        raise ValueError(f"{where}: {what} must be a device tensor (got {t.device})")
+    return t.data_ptr()
+
+
+def _caches(k_cache, v_cache, where: str):
+    """Shape ``(N, bs, Hkv, D)`` and element-type code of a K/V cache pair
+    after checking both (same shape and type, contiguous, on the device)."""
+    import torch
+    if k_cache.dim() != 4 or k_cache.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"{where}: k_cache must be a float32 or bfloat16 [num_blocks, "
+                         f"block_size, num_kv_heads, head_dim] tensor (got {k_cache.dtype}, "
+                         f"{list(k_cache.shape)})")
+    if v_cache.dtype != k_cache.dtype:
+        raise ValueError(f"{where}: v_cache must have the cache's element type {k_cache.dtype} "
+                         f"(got {v_cache.dtype})")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError(f"{where}: v_cache must have shape {list(k_cache.shape)} "
+                         f"(got {list(v_cache.shape)})")
+    _dense_ptr(k_cache, k_cache.shape, k_cache.dtype, "k_cache", where)
+    _dense_ptr(v_cache, k_cache.shape, k_cache.dtype, "v_cache", where)
+    return tuple(k_cache.shape), _dtype_code(k_cache)
+
+
+def _workspace(workspace, where: str):
+    """(pointer, bytes) of an optional device workspace (``None``: none)."""
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError(f"{where}: workspace must be a contiguous device tensor "
+                         f"(got {workspace.device})")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _decode_indices(block_tables, context_lens, seq_order, B: int, where: str):
+    """Pointers of a decode call's tables, lengths and launch order."""
+    return (_index_ptr(block_tables, B, "block_tables", where, rows=True),
+            _index_ptr(context_lens, B, "context_lens", where),
+            _index_ptr(seq_order, B, "seq_order", where))
+
+
+def _q_out(q, out, shape, dtype, where: str):
+    """Pointers of the queries and the output, both ``shape``, contiguous."""
+    return (_dense_ptr(q, shape, dtype, "q", where), _dense_ptr(out, shape, dtype, "out", where))
+
+
 def _stream_ptr(stream) -> int:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -175,15 +241,18 @@ def _stream_ptr(stream) -> int:
 
 
 def kv_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
-    """Write ``key``/``value`` ``[T, Hkv, D]`` into the caches at ``slot_mapping`` (int64)."""
-    N, bs, Hkv, D = k_cache.shape
+    """Write ``key``/``value`` ``[T, Hkv, D]`` into the caches at ``slot_mapping`` (int64).
+    Token rows may be strided; each token's ``[Hkv, D]`` must be contiguous."""
+    fn = "kv_reshape_and_cache"
     T = key.shape[0]
+    slots = _index_ptr(slot_mapping, T, "slot_mapping", fn, wide=True)
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
+    kp = _dense_ptr(key, (T, Hkv, D), k_cache.dtype, "key", fn, rows=True)
+    vp = _dense_ptr(value, (T, Hkv, D), k_cache.dtype, "value", fn, rows=True)
     _check(lib.pkv_kv_reshape_and_cache(
-        key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        _index_ptr(slot_mapping, T, "slot_mapping", "kv_reshape_and_cache", wide=True),
-        T, Hkv, D, bs, N,
+        kp, vp, k_cache.data_ptr(), v_cache.data_ptr(), slots, T, Hkv, D, bs, N,
         key.stride(0) if T else Hkv * D, value.stride(0) if T else Hkv * D,
-        _dtype_code(k_cache), _stream_ptr(stream)), "kv_reshape_and_cache")
+        dt, _stream_ptr(stream)), fn)
 
 
 def longest_first_order(context_lens) -> np.ndarray:
@@ -215,7 +284,12 @@ def stream_read(src, out, workgroups: int, stream=None) -> None:
     decode roofline.  ``out`` is a device uint32/int32 tensor of at least
     ``workgroups`` entries; entry w receives the XOR of the 32-bit words
     workgroup w read."""
-    assert out.numel() >= workgroups
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("stream_read: src must be a contiguous device tensor")
+    if (not out.is_cuda or not out.is_contiguous() or out.element_size() != 4
+            or out.numel() < workgroups):
+        raise ValueError(f"stream_read: out must be a contiguous 32-bit device tensor of at "
+                         f"least {workgroups} entries")
     _check(lib.pkv_stream_read(src.data_ptr(), src.numel() * src.element_size(), out.data_ptr(),
                                int(workgroups), _stream_ptr(stream)), "stream_read")
 
@@ -231,16 +305,15 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     ``seq_order`` an optional device int32 launch order (longest first is
     fastest, see ``longest_first_order``)."""
     fn = "paged_attention_decode"
-    N, bs, Hkv, D = k_cache.shape
-    B, Hq, _ = q.shape
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    B, Hq = q.shape[0], q.shape[1]
+    idx = _decode_indices(block_tables, context_lens, seq_order, B, fn)
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
+    qp, op = _q_out(q, out, (B, Hq, D), k_cache.dtype, fn)
+    ws_ptr, ws_bytes = _workspace(workspace, fn)
     _check(lib.pkv_paged_attention_decode(
-        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        _index_ptr(block_tables, B, "block_tables", fn, rows=True), block_tables.shape[1],
-        _index_ptr(context_lens, B, "context_lens", fn), _index_ptr(seq_order, B, "seq_order", fn),
-        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
-        ws_ptr, ws_bytes, _dtype_code(q), _stream_ptr(stream)), fn)
+        op, qp, k_cache.data_ptr(), v_cache.data_ptr(), idx[0], block_tables.shape[1], idx[1],
+        idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
+        ws_ptr, ws_bytes, dt, _stream_ptr(stream)), fn)
 
 
 def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens,
@@ -254,19 +327,18 @@ def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
     ``member_flag``: device int32 [num_seqs], nonzero for the members;
     ``workspace``: at least ``decode_workspace_bytes(..., prefix_tokens)``."""
     fn = "paged_attention_decode_shared_prefix"
-    N, bs, Hkv, D = k_cache.shape
-    B, Hq, _ = q.shape
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    B, Hq = q.shape[0], q.shape[1]
+    idx = _decode_indices(block_tables, context_lens, seq_order, B, fn)
     M = members.numel() if members is not None else 0
+    mp = _index_ptr(members, M, "members", fn) if M else None
+    fp = _index_ptr(member_flag, B, "member_flag", fn) if M else None
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
+    qp, op = _q_out(q, out, (B, Hq, D), k_cache.dtype, fn)
+    ws_ptr, ws_bytes = _workspace(workspace, fn)
     _check(lib.pkv_paged_attention_decode_shared_prefix(
-        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        _index_ptr(block_tables, B, "block_tables", fn, rows=True), block_tables.shape[1],
-        _index_ptr(context_lens, B, "context_lens", fn), _index_ptr(seq_order, B, "seq_order", fn),
-        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale),
-        _index_ptr(members, M, "members", fn) if M else None,
-        _index_ptr(member_flag, B, "member_flag", fn) if M else None, M, int(prefix_tokens), ws_ptr,
-        ws_bytes, _dtype_code(q), _stream_ptr(stream)), fn)
+        op, qp, k_cache.data_ptr(), v_cache.data_ptr(), idx[0], block_tables.shape[1], idx[1],
+        idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), mp, fp, M,
+        int(prefix_tokens), ws_ptr, ws_bytes, dt, _stream_ptr(stream)), fn)
 
 
 def paged_attention_decode_write(out, q, new_key, new_value, k_cache, v_cache, block_tables,
@@ -277,23 +349,19 @@ def paged_attention_decode_write(out, q, new_key, new_value, k_cache, v_cache, b
     position, ``context_lens[b] - 1``) gets ``new_key[b]`` / ``new_value[b]``
     (``[B, Hkv, D]``, rows may be strided) written into the caches at the slot
     its block table gives, then ``paged_attention_decode``."""
-    N, bs, Hkv, D = k_cache.shape
-    B, Hq, _ = q.shape
-    for t, nm in ((new_key, "new_key"), (new_value, "new_value")):
-        if tuple(t.shape) != (B, Hkv, D) or t.stride(2) != 1 or (Hkv > 1 and t.stride(1) != D):
-            raise ValueError(f"paged_attention_decode_write: {nm} must be [{B}, {Hkv}, {D}] "
-                             "with each sequence's row contiguous")
     fn = "paged_attention_decode_write"
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    B, Hq = q.shape[0], q.shape[1]
+    idx = _decode_indices(block_tables, context_lens, seq_order, B, fn)
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
+    qp, op = _q_out(q, out, (B, Hq, D), k_cache.dtype, fn)
+    kp = _dense_ptr(new_key, (B, Hkv, D), k_cache.dtype, "new_key", fn, rows=True)
+    vp = _dense_ptr(new_value, (B, Hkv, D), k_cache.dtype, "new_value", fn, rows=True)
+    ws_ptr, ws_bytes = _workspace(workspace, fn)
     _check(lib.pkv_paged_attention_decode_write(
-        out.data_ptr(), q.data_ptr(), new_key.data_ptr(), new_value.data_ptr(),
-        new_key.stride(0) if B else Hkv * D, new_value.stride(0) if B else Hkv * D,
-        k_cache.data_ptr(), v_cache.data_ptr(),
-        _index_ptr(block_tables, B, "block_tables", fn, rows=True), block_tables.shape[1],
-        _index_ptr(context_lens, B, "context_lens", fn), _index_ptr(seq_order, B, "seq_order", fn),
-        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size), ws_ptr,
-        ws_bytes, _dtype_code(q), _stream_ptr(stream)), fn)
+        op, qp, kp, vp, new_key.stride(0) if B else Hkv * D,
+        new_value.stride(0) if B else Hkv * D, k_cache.data_ptr(), v_cache.data_ptr(), idx[0],
+        block_tables.shape[1], idx[1], idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N,
+        float(scale), int(partition_size), ws_ptr, ws_bytes, dt, _stream_ptr(stream)), fn)
 
 
 def upload_pinned(dst, src_pinned, stream=None) -> None:
@@ -302,6 +370,10 @@ def upload_pinned(dst, src_pinned, stream=None) -> None:
     n = src_pinned.numel() * src_pinned.element_size()
     if dst.numel() * dst.element_size() != n:
         raise ValueError("upload_pinned: size mismatch")
+    if not dst.is_cuda or not dst.is_contiguous():
+        raise ValueError("upload_pinned: dst must be a contiguous device tensor")
+    if src_pinned.is_cuda or not src_pinned.is_contiguous():
+        raise ValueError("upload_pinned: src must be a contiguous pinned host tensor")
     _check(lib.pkv_upload_pinned(dst.data_ptr(), src_pinned.data_ptr(), n, _stream_ptr(stream)),
            "upload_pinned")
 
@@ -336,27 +408,25 @@ def paged_attention_prefill(out, q, query_start, max_queries_per_seq: int, k_cac
     ``q [T, Hq, D]`` are the last tokens of sequence ``b`` and attend causally
     to its paged context.  ``query_start``: device int32 ``[B + 1]``."""
     fn = "paged_attention_prefill"
-    N, bs, Hkv, D = k_cache.shape
-    T, Hq, _ = q.shape
+    T, Hq = q.shape[0], q.shape[1]
     B = context_lens.shape[0]
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    qs = _index_ptr(query_start, B + 1, "query_start", fn)
+    idx = _decode_indices(block_tables, context_lens, seq_order, B, fn)
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
+    qp, op = _q_out(q, out, (T, Hq, D), k_cache.dtype, fn)
+    ws_ptr, ws_bytes = _workspace(workspace, fn)
     _check(lib.pkv_paged_attention_prefill(
-        out.data_ptr(), q.data_ptr(), _index_ptr(query_start, B + 1, "query_start", fn), T,
-        int(max_queries_per_seq), k_cache.data_ptr(), v_cache.data_ptr(),
-        _index_ptr(block_tables, B, "block_tables", fn, rows=True), block_tables.shape[1],
-        _index_ptr(context_lens, B, "context_lens", fn), _index_ptr(seq_order, B, "seq_order", fn),
-        int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size), ws_ptr,
-        ws_bytes, _dtype_code(q), _stream_ptr(stream)), fn)
+        op, qp, qs, T, int(max_queries_per_seq), k_cache.data_ptr(), v_cache.data_ptr(), idx[0],
+        block_tables.shape[1], idx[1], idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N,
+        float(scale), int(partition_size), ws_ptr, ws_bytes, dt, _stream_ptr(stream)), fn)
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     """``cache[dst] = cache[src]`` for each row ``(src, dst)`` of int64 ``pairs [P, 2]``."""
-    N, bs, Hkv, D = k_cache.shape
-    _check(lib.pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(),
-                               _index_ptr(pairs, 0, "pairs", "copy_blocks", wide=True, cols=2),
-                               pairs.shape[0], N, bs, Hkv, D, _dtype_code(k_cache),
-                               _stream_ptr(stream)), "copy_blocks")
+    pp = _index_ptr(pairs, 0, "pairs", "copy_blocks", wide=True, cols=2)
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, "copy_blocks")
+    _check(lib.pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pp, pairs.shape[0], N, bs,
+                               Hkv, D, dt, _stream_ptr(stream)), "copy_blocks")
 
 
 def swap_blocks(k_cache, v_cache, k_host, v_host, pairs, direction: int, stream=None) -> None:
@@ -364,18 +434,19 @@ def swap_blocks(k_cache, v_cache, k_host, v_host, pairs, direction: int, stream=
     ``[Nh, bs, Hkv, D]`` (torch CPU tensors from ``pin_memory()``):
     SWAP_OUT copies device block ``src`` to host block ``dst`` for each row of
     ``pairs`` (device int64 ``[P, 2]``), SWAP_IN host ``src`` to device ``dst``."""
-    N, bs, Hkv, D = k_cache.shape
+    pp = _index_ptr(pairs, 0, "pairs", "swap_blocks", wide=True, cols=2)
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, "swap_blocks")
     Nh = k_host.shape[0]
     if tuple(k_host.shape[1:]) != (bs, Hkv, D) or k_host.shape != v_host.shape:
         raise ValueError("host pools must be [num_host_blocks, block_size, Hkv, D]")
     if k_host.dtype != k_cache.dtype or v_host.dtype != k_cache.dtype:
         raise TypeError("host pools must have the cache dtype")
+    if (k_host.is_cuda or v_host.is_cuda or not k_host.is_contiguous()
+            or not v_host.is_contiguous()):
+        raise ValueError("swap_blocks: host pools must be contiguous pinned host tensors")
     _check(lib.pkv_swap_blocks(k_cache.data_ptr(), v_cache.data_ptr(), k_host.data_ptr(),
-                               v_host.data_ptr(),
-                               _index_ptr(pairs, 0, "pairs", "swap_blocks", wide=True, cols=2),
-                               pairs.shape[0], N, Nh, bs,
-                               Hkv, D, _dtype_code(k_cache), int(direction), _stream_ptr(stream)),
-           "swap_blocks")
+                               v_host.data_ptr(), pp, pairs.shape[0], N, Nh, bs, Hkv, D, dt,
+                               int(direction), _stream_ptr(stream)), "swap_blocks")
 
 
 # ------------------------------------------------------------------ allocator

@@ -427,3 +427,45 @@ def test_wrappers_refuse_index_arrays_that_are_not_int32_device_tensors():
                       P.SWAP_OUT)
     with pytest.raises(ValueError, match="int64"):
         P._index_ptr(torch.zeros(3, 2, dtype=torch.int32), 0, "pairs", "f", wide=True, cols=2)
+
+
+def test_wrappers_refuse_dense_operands_of_the_wrong_type_shape_layout_or_device():
+    """q, out, caches, new keys/values and the workspace reach the kernels as
+    raw addresses sized by the cache's element type and shape: the binding
+    refuses another element type, another shape, a non-contiguous layout
+    and host memory, each with its own message, before any library call."""
+    import torch
+    import paged_kv_cache_292_amd as P
+
+    bf = torch.bfloat16
+    with pytest.raises(ValueError, match="f: q must have the cache's element type"):
+        P._dense_ptr(torch.zeros(2, 4, 64), (2, 4, 64), bf, "q", "f")
+    with pytest.raises(ValueError, match=r"f: out must have shape \[2, 4, 64\]"):
+        P._dense_ptr(torch.zeros(2, 4, 128, dtype=bf), (2, 4, 64), bf, "out", "f")
+    with pytest.raises(ValueError, match="f: q must be contiguous"):
+        P._dense_ptr(torch.zeros(4, 2, 64, dtype=bf).transpose(0, 1), (2, 4, 64), bf, "q", "f")
+    with pytest.raises(ValueError, match="f: q must be a device tensor"):
+        P._dense_ptr(torch.zeros(2, 4, 64, dtype=bf), (2, 4, 64), bf, "q", "f")
+    # strided token rows with contiguous [Hkv, D] parts pass the layout check
+    rows = torch.zeros(3, 2, 2, 64, dtype=bf)[:, 0]
+    with pytest.raises(ValueError, match="key must be a device tensor"):
+        P._dense_ptr(rows, (3, 2, 64), bf, "key", "f", rows=True)
+    with pytest.raises(ValueError, match="key must be row-contiguous"):
+        P._dense_ptr(torch.zeros(3, 64, 2, dtype=bf).transpose(1, 2), (3, 2, 64), bf, "key", "f",
+                     rows=True)
+    # cache pairs: rank and element type, then equal shape and type, then device
+    with pytest.raises(ValueError, match="k_cache must be a float32 or bfloat16"):
+        P._caches(torch.zeros(4, 16, 64), torch.zeros(4, 16, 64), "f")
+    with pytest.raises(ValueError, match="v_cache must have the cache's element type"):
+        P._caches(torch.zeros(4, 16, 2, 64), torch.zeros(4, 16, 2, 64, dtype=bf), "f")
+    with pytest.raises(ValueError, match=r"v_cache must have shape \[4, 16, 2, 64\]"):
+        P._caches(torch.zeros(4, 16, 2, 64), torch.zeros(5, 16, 2, 64), "f")
+    with pytest.raises(ValueError, match="k_cache must be a device tensor"):
+        P._caches(torch.zeros(4, 16, 2, 64), torch.zeros(4, 16, 2, 64), "f")
+    with pytest.raises(ValueError, match="workspace must be a contiguous device tensor"):
+        P._workspace(torch.zeros(64, dtype=torch.uint8), "f")
+    assert P._workspace(None, "f") == (None, 0)
+    with pytest.raises(ValueError, match="upload_pinned: dst must be a contiguous device"):
+        P.upload_pinned(torch.zeros(16, dtype=torch.uint8), torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="stream_read: src must be a contiguous device"):
+        P.stream_read(torch.zeros(16, dtype=torch.uint8), torch.zeros(1, dtype=torch.int32), 1)

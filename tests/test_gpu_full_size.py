@@ -1,0 +1,248 @@
+"""Full-size parity of exactly the calls the benchmark times, on every
+output row.
+
+Each test sets up the first timed step of ``bench.py --shape i`` the way the
+benchmark does: the pool sized with the benchmark's growth room, tables
+padded to the width of the last step, the longest-first launch order from
+the allocator, automatic partitioning, and for the LLaMA-13B batch the
+decode call that also writes the step's new tokens.  The product allocator's
+slots, tables, lengths and order must equal the oracle allocator's (and a
+stable longest-first sort) bit for bit; then every (sequence, query head)
+row of every launch is compared with the fp64 oracle
+(``oracle.attention.paged_decode``; chunked prefill: every query row of the
+longest, the shortest and one more sequence, all heads) at the bf16
+tolerance (max-abs 2e-2, normwise 1e-2 per row) or the fp32 one (1e-5
+relative per row).  Unused tail slots hold NaN, so a read outside a
+context fails.  Attention over a paged cache: "vLLM in Production …",
+section "PagedAttention — Virtual Memory for the KV Cache"."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle.allocator as OAL
+import oracle.attention as OA
+import oracle.cache_write as OC
+import workloads as W
+from gpu_cases import assert_close, from_dev, log, poison_unused_tail, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+import paged_kv_cache_292_amd as P  # noqa: E402  (fails loudly when the library is missing)
+
+# bench.py defaults: 5 warm-up + 50 timed steps
+BENCH_STEPS = 55
+
+
+def _longest_first(ctx: np.ndarray) -> np.ndarray:
+    """Indices by context length, longest first, ties by index."""
+    return np.argsort(-np.asarray(ctx, dtype=np.int64), kind="stable").astype(np.int32)
+
+
+@dataclasses.dataclass
+class BenchStep:
+    s: W.DecodeShape
+    wl: W.Workload
+    tables: np.ndarray
+    ctx: np.ndarray
+    order: np.ndarray
+    slots: np.ndarray        # the step's new slots (empty without new tokens)
+    k_before: np.ndarray     # host caches before the step's cache write
+    v_before: np.ndarray
+    k_after: np.ndarray      # oracle caches after it
+    v_after: np.ndarray
+
+
+def bench_first_step(idx: int) -> BenchStep:
+    """Step 0 of ``bench.py --shape idx`` on both allocators."""
+    s = W.shape(idx)
+    step_tok = s.chunk if s.chunk else (1 if s.new_tokens else 0)
+    wl = W.make_workload(s, extra_tokens=BENCH_STEPS * step_tok)
+    B, bs = s.num_seqs, s.block_size
+    final_ctx = wl.ctx + (BENCH_STEPS - 1) * step_tok
+    max_blocks = int(((final_ctx + bs - 1) // bs).max())
+    o = OAL.BlockAllocator(wl.num_blocks, bs, wl.free_order)
+    o.replay(wl.ops)
+    p = P.Allocator(wl.num_blocks, bs, wl.free_order)
+    p.replay(wl.ops)
+    seqs = np.arange(B, dtype=np.int64)
+    if s.new_tokens:
+        slots_o = np.array([o.append(b, 1)[0] for b in range(B)], dtype=np.int64)
+        slots_p = np.empty(B, np.int64)
+        tables_p = np.empty((B, max_blocks), np.int32)
+        ctx_p = np.empty(B, np.int32)
+        order_p = np.empty(B, np.int32)
+        mx = p.decode_step_prepare(seqs, max_blocks, slots_p, tables_p, ctx_p, order_out=order_p)
+    else:
+        if s.chunk:
+            slots_o = np.array([x for b in range(B) for x in o.append(b, s.chunk)], np.int64)
+            slots_p = p.append_tokens(seqs, [s.chunk] * B)
+        else:
+            slots_o = slots_p = np.zeros(0, np.int64)
+        tables_p, ctx_p = p.build_block_tables(seqs, max_blocks, pad=-1)
+        order_p = P.longest_first_order(ctx_p)
+        mx = int(ctx_p.max())
+    p.close()
+    tables_o, ctx_o = o.build_block_tables(list(range(B)), max_blocks, pad=-1)
+    assert np.array_equal(slots_o, slots_p), "slots differ from the oracle allocator's"
+    assert np.array_equal(tables_o, tables_p), "block tables differ from the oracle allocator's"
+    assert np.array_equal(ctx_o, ctx_p) and mx == int(ctx_o.max())
+    assert np.array_equal(order_p, _longest_first(ctx_o)), "launch order"
+    assert np.array_equal(ctx_o, wl.ctx)
+
+    kc, vc = wl.k_cache, wl.v_cache
+    poison_unused_tail(kc, tables_o, ctx_o, s.dtype)
+    poison_unused_tail(vc, tables_o, ctx_o, s.dtype)
+    if len(slots_o):  # the step's slots hold garbage until written
+        nan = np.float32(np.nan) if s.dtype == "f32" else W.BF16_NAN_BITS
+        kc[slots_o // bs, slots_o % bs] = nan
+        vc[slots_o // bs, slots_o % bs] = nan
+        ka, va = OC.reshape_and_cache(wl.new_k, wl.new_v, kc, vc, slots_o)
+    else:
+        ka, va = kc, vc
+    return BenchStep(s, wl, tables_o, ctx_o, order_p, slots_o, kc, vc, ka, va)
+
+
+class Dev:
+    """The step's device tensors."""
+
+    def __init__(self, st: BenchStep, write: bool):
+        s = st.s
+        self.q = to_dev(st.wl.q, s.dtype)
+        self.k = to_dev(st.k_before, s.dtype)
+        self.v = to_dev(st.v_before, s.dtype)
+        self.tables = torch.from_numpy(st.tables).cuda()
+        self.ctx = torch.from_numpy(st.ctx.astype(np.int32)).cuda()
+        self.order = torch.from_numpy(st.order).cuda()
+        self.max_ctx = int(st.ctx.max())
+        if st.wl.new_k is not None:
+            self.new_k = to_dev(st.wl.new_k, s.dtype)
+            self.new_v = to_dev(st.wl.new_v, s.dtype)
+            if write:  # the separate cache write, as bench.py --separate-write does
+                P.kv_reshape_and_cache(self.new_k, self.new_v, self.k, self.v,
+                                       torch.from_numpy(st.slots).cuda())
+        torch.cuda.synchronize()
+
+    def workspace(self, s, part):
+        n = P.decode_workspace_bytes(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                     s.block_size, self.max_ctx, part,
+                                     P.F32 if s.dtype == "f32" else P.BF16)
+        return torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+
+
+def _decode(st, d, part):
+    s = st.s
+    out = torch.empty_like(d.q)
+    P.paged_attention_decode(out, d.q, d.k, d.v, d.tables, d.ctx, d.max_ctx, s.scale, part,
+                             d.workspace(s, part), seq_order=d.order)
+    torch.cuda.synchronize()
+    return OA.widen(from_dev(out, s.dtype), s.dtype)
+
+
+def _oracle(st):
+    s = st.s
+    return OA.paged_decode(st.wl.q, st.k_after, st.v_after, st.tables, st.ctx, s.scale, s.dtype)
+
+
+def _bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_full_tiny_and_llama7b(idx):
+    st = bench_first_step(idx)
+    log(f"full size {st.s.name}: B={st.s.num_seqs}, automatic partitioning, longest first")
+    ref = _oracle(st)
+    d = Dev(st, write=False)
+    assert_close(_decode(st, d, P.PARTITION_AUTO), ref, st.s.dtype, f"{st.s.name} full, AUTO")
+
+
+def test_full_llama13b_fused_write():
+    """The benchmark's gate call: cache write and decode in one launch, all
+    128 sequences, longest-first order, automatic partitioning.  Caches
+    bit-exact against the oracle's cache write, every row within tolerance."""
+    st = bench_first_step(2)
+    s = st.s
+    log(f"full size {s.name}: fused write + decode, B={s.num_seqs}")
+    ref = _oracle(st)
+    d = Dev(st, write=False)
+    out = torch.empty_like(d.q)
+    P.paged_attention_decode_write(out, d.q, d.new_k, d.new_v, d.k, d.v, d.tables, d.ctx,
+                                   d.max_ctx, s.scale, P.PARTITION_AUTO,
+                                   d.workspace(s, P.PARTITION_AUTO), seq_order=d.order)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(from_dev(d.k, s.dtype)), _bits(st.k_after)), "K cache after write"
+    assert np.array_equal(_bits(from_dev(d.v, s.dtype)), _bits(st.v_after)), "V cache after write"
+    assert_close(OA.widen(from_dev(out, s.dtype), s.dtype), ref, s.dtype,
+                 f"{s.name} full, fused write, AUTO")
+    # the separate write then decode (bench.py --separate-write), and single pass
+    d2 = Dev(st, write=True)
+    assert_close(_decode(st, d2, P.PARTITION_AUTO), ref, s.dtype, f"{s.name} full, separate write")
+    assert_close(_decode(st, d2, 2048), ref, s.dtype, f"{s.name} full, 2048-token partitions")
+
+
+def test_full_gqa_prefix():
+    """The GQA batch: automatic partitioning, and the shared-prefix call with
+    its 128 members and 1,024-token prefix."""
+    st = bench_first_step(3)
+    s = st.s
+    log(f"full size {s.name}: B={s.num_seqs}, AUTO and shared prefix")
+    ref = _oracle(st)
+    d = Dev(st, write=False)
+    assert_close(_decode(st, d, P.PARTITION_AUTO), ref, s.dtype, f"{s.name} full, AUTO")
+    flag = np.zeros(s.num_seqs, dtype=np.int32)
+    flag[st.wl.sharers] = 1
+    members = torch.from_numpy(st.wl.sharers.astype(np.int32)).cuda()
+    out = torch.empty_like(d.q)
+    P.paged_attention_decode_shared_prefix(out, d.q, d.k, d.v, d.tables, d.ctx, d.max_ctx,
+                                           s.scale, members, torch.from_numpy(flag).cuda(),
+                                           s.shared_prefix_tokens,
+                                           d.workspace(s, s.shared_prefix_tokens),
+                                           seq_order=d.order)
+    torch.cuda.synchronize()
+    assert_close(OA.widen(from_dev(out, s.dtype), s.dtype), ref, s.dtype,
+                 f"{s.name} full, shared prefix")
+
+
+def test_full_long_splitk():
+    """The long-context batch at automatic partitioning and at its own
+    512-token partitions (32 to 64 per sequence)."""
+    st = bench_first_step(4)
+    s = st.s
+    log(f"full size {s.name}: B={s.num_seqs}, AUTO and 512-token partitions")
+    ref = _oracle(st)
+    d = Dev(st, write=False)
+    assert_close(_decode(st, d, P.PARTITION_AUTO), ref, s.dtype, f"{s.name} full, AUTO")
+    assert_close(_decode(st, d, 512), ref, s.dtype, f"{s.name} full, 512-token partitions")
+
+
+def test_full_prefill_chunk():
+    """The chunked-prefill step (16 sequences x 512 new tokens, 40 heads):
+    the chunk's cache write, then prefill at automatic partitioning in
+    longest-first order; every query row of three whole sequences, all heads,
+    against the oracle."""
+    st = bench_first_step(5)
+    s = st.s
+    B, C = s.num_seqs, s.chunk
+    log(f"full size {s.name}: B={B} x {C} queries")
+    d = Dev(st, write=False)
+    P.kv_reshape_and_cache(d.new_k, d.new_v, d.k, d.v, torch.from_numpy(st.slots).cuda())
+    starts = np.arange(B + 1, dtype=np.int32) * C
+    out = torch.empty((B * C, s.num_q_heads, s.head_dim), dtype=torch.bfloat16, device="cuda")
+    wsb = P.prefill_workspace_bytes(B * C, s.num_q_heads, s.head_dim, d.max_ctx,
+                                    P.PARTITION_AUTO)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    P.paged_attention_prefill(out, d.q, torch.from_numpy(starts).cuda(), C, d.k, d.v, d.tables,
+                              d.ctx, d.max_ctx, s.scale, P.PARTITION_AUTO, ws, seq_order=d.order)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(from_dev(d.k, s.dtype)), _bits(st.k_after)), "K cache after write"
+    got = OA.widen(from_dev(out, "bf16"), "bf16")
+    pick = sorted({int(np.argmax(st.ctx)), int(np.argmin(st.ctx)), B // 2})
+    for b in pick:
+        rows = slice(b * C, (b + 1) * C)
+        ref = OA.paged_prefill(st.wl.q[rows], st.k_after, st.v_after, st.tables[b:b + 1],
+                               st.ctx[b:b + 1], np.array([0, C]), s.scale, "bf16")
+        assert_close(got[rows], ref, "bf16", f"prefill sequence {b} (context {st.ctx[b]})")
