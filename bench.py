@@ -57,6 +57,9 @@ def _args():
                     help="decode a batch with a shared prefix through "
                          "paged_attention_decode_shared_prefix (the prefix partition computed "
                          "once per tile of sharing sequences)")
+    ap.add_argument("--prefix-tokens", type=int, default=None,
+                    help="length of the shared prefix of a batch with sharing (the GQA batch: "
+                         "1024 as specified); sharers are drawn among longer sequences")
     ap.add_argument("--prefix-cache", action="store_true",
                     help="measure admitting requests that share a cached 2,000-token system "
                          "prompt, against the same requests computed in full")
@@ -479,6 +482,10 @@ def main() -> int:
     torch.cuda.set_device(dev)
     P.set_decode_path({"auto": P.PATH_AUTO, "valu": P.PATH_VALU, "mfma": P.PATH_MFMA}[args.path])
     s = W.shape(args.shape)
+    if args.prefix_tokens is not None:
+        if not s.num_sharers:
+            raise SystemExit("--prefix-tokens needs a batch with a shared prefix (--shape 3)")
+        s = W.shape(args.shape, shared_prefix_tokens=args.prefix_tokens)
     total_steps = args.warmup + args.steps
     step_new = 1 if s.new_tokens else 0
     chunk = s.chunk  # > 0: a chunked-prefill step of this many tokens per sequence
@@ -527,10 +534,9 @@ def main() -> int:
                                             dt_code)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     shared = bool(args.shared_prefix) and not chunk
-    if shared:
-        flag = np.zeros(B, dtype=np.int32)
-        flag[wl.sharers] = 1
-        d_members = torch.from_numpy(wl.sharers.astype(np.int32)).to(dev)
+    if shared:  # the members, from the allocator's tables
+        members, flag = alloc.shared_prefix_members(seqs, s.shared_prefix_tokens)
+        d_members = torch.from_numpy(members).to(dev)
         d_member_flag = torch.from_numpy(flag).to(dev)
     part_used = (P.prefill_partition_size(B, chunk, Hq, Hkv, max_ctx_final, args.partition)
                  if chunk else
@@ -737,6 +743,7 @@ def main() -> int:
             "partition_size": part_used, "kv_bytes_per_step": int(kv_t // K),
             "decode_path": args.path, "launch_order": args.order, "chunk_tokens": chunk,
             "shared_prefix_decode": shared,
+            "shared_prefix_tokens": s.shared_prefix_tokens, "num_sharers": s.num_sharers,
         },
         "roofline": {
             "kernel": ("paged_attention_decode" + ("_write (cache write fused)" if fused_write else "")

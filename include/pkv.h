@@ -62,7 +62,13 @@ const char* pkv_version(void);
 /* ------------------------------------------------------------------------
  * Cache write: store new tokens' keys and values through a slot mapping.
  *
- * Token i's rows key[i] and value[i] (each [num_kv_heads, head_dim]) go to
+ * A sequence's cache fills one token at a time, each token's K/V going into
+ * the block its table names for that position ("vLLM in Production …",
+ * section "PagedAttention — Virtual Memory for the KV Cache": blocks are
+ * allocated on demand as tokens arrive and may sit anywhere in memory;
+ * "What Is vLLM …", section "How does PagedAttention work?": a position
+ * lives in the physical block the table gives for it, at its offset inside
+ * that block).  Token i's rows key[i] and value[i] (each [num_kv_heads, head_dim]) go to
  * row (slot % block_size) of physical block (slot / block_size), where
  * slot = slot_mapping[i] was handed out by the block allocator for that
  * token's position.  A negative slot marks a padding token and is skipped;
@@ -93,6 +99,14 @@ pkv_status pkv_kv_reshape_and_cache(const void* key, const void* value,
 /* ------------------------------------------------------------------------
  * Paged decode attention: one query token per sequence.
  *
+ * Each new token attends to the keys and values of every earlier token of
+ * its sequence and to its own ("vLLM in Production …", section "The KV Cache
+ * and the 60–80% Memory Tax"); those K/V rows sit in fixed-size blocks
+ * anywhere in the pool, reached through the sequence's block table (same
+ * page, section "PagedAttention — Virtual Memory for the KV Cache"; "What Is
+ * vLLM …", section "How does PagedAttention work?": the block holding a
+ * position is looked up, then indexed into).
+ *
  * For sequence b and query head h (kv head g = h / (num_q_heads /
  * num_kv_heads)): out[b, h] = softmax(scale * K_b q[b, h]) V_b, where K_b
  * and V_b are the context_lens[b] rows of kv head g gathered through the
@@ -108,8 +122,9 @@ pkv_status pkv_kv_reshape_and_cache(const void* key, const void* value,
  * partition_size == 0: single pass per sequence.
  * partition_size == PKV_PARTITION_AUTO (-1): the library chooses from
  * max_context_len and the kernel that runs (pkv_decode_partition_size tells
- * the choice; the decode-path setting must be the same when sizing the
- * workspace and when calling).
+ * the choice).  pkv_decode_workspace_bytes(..., PKV_PARTITION_AUTO, ...)
+ * covers every automatic choice of every kernel, so the workspace does not
+ * depend on the decode-path setting.
  *
  * out           device, [num_seqs, num_q_heads, head_dim].
  * q             device, [num_seqs, num_q_heads, head_dim].
@@ -136,9 +151,17 @@ pkv_status pkv_kv_reshape_and_cache(const void* key, const void* value,
  *            G = num_q_heads / num_kv_heads being 1..16 for bf16 and
  *            1, 2, 4 or 8 for f32; partition_size a multiple of block_size
  *            (or 0 / -1); num_seqs <= 65535.
- * Kernels: a vector-ALU kernel for G = 1 (and f32), a matrix-core kernel
- * (bf16 MFMA for q.K, fp32 MFMA for the weighted sum of V) for grouped
- * query heads; see pkv_set_decode_path.
+ * Kernels (PKV_PATH_AUTO): f32, and bf16 with G <= 2, run on the vector
+ * ALUs: fp32 dot products (bf16 pairs widened by v_dot2), fp32 softmax and
+ * fp32 weighted sum of V; rounding only in the fp32 arithmetic and the
+ * output store.  bf16 with G >= 3 runs on the matrix cores: q.K on bf16
+ * MFMA with fp32 accumulation; the softmax weights p (fp32, each at most
+ * 2^8 times the weight of the running maximum) are rounded to bf16 for the
+ * P.V product, a bf16 MFMA accumulating in fp32, while the softmax sum adds
+ * the unrounded fp32 p.  Rounding p (relative error at most 2^-9 per weight)
+ * changes an output element by at most 2^-9 * sum_t p_t |v_t| / sum_t p_t
+ * <= 2^-9 * max_t |v_t|, before the output's own rounding (2^-9 relative
+ * for bf16).  See pkv_set_decode_path for forcing one kernel.
  * ---------------------------------------------------------------------- */
 #define PKV_PARTITION_AUTO (-1)
 
@@ -371,6 +394,14 @@ pkv_status pkv_swap_blocks(void* k_cache, void* v_cache, void* k_host, void* v_h
 /* ------------------------------------------------------------------------
  * Host block allocator (host memory only; single-threaded use).
  *
+ * The pool of fixed-size blocks, the per-sequence block tables mapping
+ * logical blocks to physical ones like a page table, and growth one block
+ * at a time ("vLLM in Production …", section "PagedAttention — Virtual Memory
+ * for the KV Cache"); only a sequence's last block is partly empty
+ * ("Serving models with vLLM", section "How it works: PagedAttention");
+ * blocks shared between sequences carry reference counts ("What Is vLLM …",
+ * section "How does PagedAttention work?", memory-sharing step).
+ *
  * Fixed-size blocks are handed out one at a time as a sequence grows; a
  * sequence's table lists its physical blocks in logical order and token
  * pos is stored at slot table[pos / block_size] * block_size +
@@ -381,22 +412,34 @@ pkv_status pkv_swap_blocks(void* k_cache, void* v_cache, void* k_host, void* v_h
  * ---------------------------------------------------------------------- */
 typedef struct pkv_allocator pkv_allocator;
 
-/* Creates an allocator; *out receives the handle (library-owned memory,
- * released by pkv_allocator_destroy). */
+/* Creates an allocator over a pool of num_blocks blocks of block_size
+ * tokens ("vLLM in Production …", section "PagedAttention — Virtual Memory
+ * for the KV Cache": the cache is cut into fixed-size blocks); *out receives
+ * the handle (library-owned memory, released by pkv_allocator_destroy).
+ * PKV_ERR_INVALID_ARG for a negative num_blocks, a non-positive block_size
+ * or a free_order that is not a permutation of 0..num_blocks-1. */
 pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_size,
                                 const int32_t* free_order, pkv_allocator** out);
 void pkv_allocator_destroy(pkv_allocator* a);
 
-/* New empty sequence; PKV_ERR_INVALID_ARG if the id exists. */
+/* New empty sequence: no block is reserved up front ("Serving models with
+ * vLLM", section "How it works: PagedAttention": blocks are allocated on
+ * demand).  PKV_ERR_INVALID_ARG if the id exists. */
 pkv_status pkv_seq_add(pkv_allocator* a, int64_t seq_id);
 
 /* dst (existing, empty) shares the blocks holding src's first num_tokens
- * tokens (each block's reference count + 1).  num_tokens must be a multiple
- * of block_size or src's whole length. */
+ * tokens (each block's reference count + 1): sequences with a common prefix
+ * point at the same physical blocks ("What Is vLLM …", section "How does
+ * PagedAttention work?", memory-sharing step).  num_tokens must be a
+ * multiple of block_size or src's whole length (PKV_ERR_INVALID_ARG);
+ * PKV_ERR_NOT_FOUND for an unknown id. */
 pkv_status pkv_seq_fork_prefix(pkv_allocator* a, int64_t src, int64_t dst,
                                int32_t num_tokens);
 
-/* Grows seq_id by num_tokens; slots_out (host, int64 [num_tokens], may be
+/* Grows seq_id by num_tokens, opening a new block only when the last one is
+ * full ("vLLM in Production …", section "PagedAttention — Virtual Memory for
+ * the KV Cache": blocks are added one at a time as tokens arrive, so no
+ * final length is guessed); slots_out (host, int64 [num_tokens], may be
  * NULL) receives their slots.  PKV_ERR_OUT_OF_BLOCKS if the pool is short,
  * PKV_ERR_SHARED_WRITE if a token would land in a block another sequence
  * holds; both leave the allocator unchanged. */
@@ -426,10 +469,16 @@ pkv_status pkv_append_tokens_cow(pkv_allocator* a, const int64_t* seq_ids,
                                  int64_t* slots_out, int64_t* copy_pairs_out,
                                  int32_t max_pairs, int32_t* num_pairs_out);
 
-/* Releases the sequence; blocks whose count drops to zero are freed. */
+/* Releases the sequence; blocks whose reference count drops to zero are
+ * freed ("What Is vLLM …", section "How does PagedAttention work?",
+ * memory-sharing step: a shared block stays while any holder remains).
+ * PKV_ERR_NOT_FOUND for an unknown id. */
 pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq_id);
 
-/* tables_out (host, int32 [num_seqs, max_blocks_per_seq]) receives each
+/* The block tables the attention calls read ("vLLM in Production …",
+ * section "PagedAttention — Virtual Memory for the KV Cache": a
+ * per-sequence table from logical to physical blocks).
+ * tables_out (host, int32 [num_seqs, max_blocks_per_seq]) receives each
  * sequence's block table padded with pad_value; context_lens_out (host,
  * int32 [num_seqs], may be NULL) their lengths.  PKV_ERR_INVALID_ARG if a
  * sequence has more than max_blocks_per_seq blocks. */
@@ -529,13 +578,74 @@ pkv_status pkv_seq_add_prompt(pkv_allocator* a, int64_t seq_id, const int32_t* t
 pkv_status pkv_prefix_cache_stats(const pkv_allocator* a, int64_t* lookups, int64_t* hits,
                                   int32_t* num_cached_blocks);
 
+/* Free blocks of the pool (the unused share of the KV-cache memory). */
 int32_t pkv_num_free_blocks(const pkv_allocator* a);
-/* Reference count of a block (0 = free), -1 for an id outside the pool. */
+/* Reference count of a block (0 = free), -1 for an id outside the pool: the
+ * number of sequences whose tables hold it ("What Is vLLM …", section "How
+ * does PagedAttention work?", memory-sharing step). */
 int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block_id);
 /* Length in tokens of a sequence, -1 if unknown. */
 int64_t pkv_seq_context_len(const pkv_allocator* a, int64_t seq_id);
 /* Number of blocks of a sequence (device or host), -1 if unknown. */
 int32_t pkv_seq_num_blocks(const pkv_allocator* a, int64_t seq_id);
+
+/* The shared-prefix members of a batch, derived from the tables ("What Is
+ * vLLM …", section "How does PagedAttention work?", memory-sharing step:
+ * sequences with a common prefix point at the same physical blocks).  Among
+ * seq_ids (distinct, resident), the sequences longer than prefix_tokens
+ * whose first prefix_tokens / block_size blocks are the same physical blocks
+ * form a group; the largest group of at least two (the one met first in
+ * seq_ids order on a tie) is reported: members_out (host int32 [num_seqs])
+ * receives its positions in seq_ids, ascending, *num_members_out their
+ * count (0 if no two sequences share), member_flag_out (host int32
+ * [num_seqs]) 1 for the members and 0 otherwise: the members / member_flag
+ * arguments of pkv_paged_attention_decode_shared_prefix for a batch in
+ * seq_ids order.  PKV_ERR_INVALID_ARG (prefix_tokens not a positive multiple
+ * of the block size, a repeated id), PKV_ERR_NOT_FOUND, PKV_ERR_SWAPPED. */
+pkv_status pkv_shared_prefix_members(const pkv_allocator* a, const int64_t* seq_ids,
+                                     int32_t num_seqs, int32_t prefix_tokens,
+                                     int32_t* members_out, int32_t* member_flag_out,
+                                     int32_t* num_members_out);
+
+/* ------------------------------------------------------------------------
+ * Pool size from a memory budget: the memory left for the KV cache becomes
+ * blocks ("vLLM in Production …", section "Scaling Up — Tensor Parallelism
+ * and Engine Args": what the memory-utilization setting leaves after the
+ * weights becomes KV-cache blocks).  One block id covers block_size tokens
+ * of K and of V in each of num_layers layers, i.e. 2 * num_layers *
+ * block_size * num_kv_heads * head_dim elements; the result is
+ * floor(bytes / that size in bytes), at most INT32_MAX (0 if one block does
+ * not fit, or its size overflows 64 bits), -1 for a non-positive size or an
+ * unknown dtype.
+ * ---------------------------------------------------------------------- */
+int32_t pkv_blocks_for_budget(size_t bytes, int32_t num_layers, int32_t block_size,
+                              int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype);
+
+/* ------------------------------------------------------------------------
+ * Debug validator of a decode call's index arrays, on host copies: the
+ * kernels never fault on a bad id (an id outside the pool reads block 0, a
+ * length beyond max_context_len is clamped, members are trusted), so such
+ * inputs return PKV_OK with a meaningless result.  This call returns
+ * PKV_ERR_INVALID_ARG, its message naming the first bad entry, unless
+ *   - 0 <= context_lens[b] <= min(max_context_len,
+ *     max_blocks_per_seq * block_size) for every b;
+ *   - every table entry a context reads (the first ceil(context_lens[b] /
+ *     block_size) of row b) lies in [0, num_blocks);
+ *   - seq_order (may be NULL) is a permutation of 0..num_seqs-1;
+ *   - with num_members > 0: members are distinct indices, member_flag is
+ *     nonzero exactly for them, every member's context is longer than
+ *     prefix_tokens (a positive multiple of block_size), and every member's
+ *     first prefix_tokens / block_size table entries equal the first
+ *     member's.
+ * All arrays are host int32: block_tables [num_seqs, max_blocks_per_seq],
+ * context_lens, seq_order, member_flag [num_seqs], members [num_members].
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_validate_decode_inputs(const int32_t* block_tables, int32_t num_seqs,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      const int32_t* seq_order, int32_t max_context_len,
+                                      int32_t block_size, int32_t num_blocks,
+                                      const int32_t* members, const int32_t* member_flag,
+                                      int32_t num_members, int32_t prefix_tokens);
 
 #ifdef __cplusplus
 }

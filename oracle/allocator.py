@@ -399,6 +399,30 @@ class BlockAllocator:
             ctx[i] = self.lengths[s]
         return tables, ctx
 
+    def shared_prefix_members(self, seqs: Sequence[int], prefix_tokens: int) -> List[int]:
+        """Positions in ``seqs`` of the sequences that share a prefix: longer
+        than ``prefix_tokens`` and holding the same physical blocks for its
+        first ``prefix_tokens // block_size`` blocks ("What Is vLLM …",
+        memory-sharing step).  Sequences are grouped by that block list; the
+        largest group of at least two is returned (the first met on a tie),
+        else an empty list."""
+        if prefix_tokens <= 0 or prefix_tokens % self.block_size:
+            raise InvalidArg("prefix_tokens must be a positive multiple of the block size")
+        if len(set(seqs)) != len(seqs):
+            raise InvalidArg("a sequence is listed twice")
+        for s in seqs:
+            self._resident(s)
+        nb = prefix_tokens // self.block_size
+        groups: Dict[tuple, List[int]] = {}
+        for i, s in enumerate(seqs):
+            if self.lengths[s] > prefix_tokens:
+                groups.setdefault(tuple(self.tables[s][:nb]), []).append(i)
+        best: List[int] = []
+        for g in groups.values():  # insertion order: first met wins a tie
+            if len(g) >= 2 and len(g) > len(best):
+                best = g
+        return best
+
     # -- replay of a workload's op list -------------------------------------
     def replay(self, ops: Iterable[tuple]) -> None:
         for op in ops:

@@ -24,6 +24,7 @@ __all__ = [
     "paged_attention_prefill", "prefill_workspace_bytes", "prefill_partition_size",
     "swap_blocks", "SWAP_OUT", "SWAP_IN",
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
+    "blocks_for_budget", "validate_decode_inputs",
 ]
 
 LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
@@ -98,6 +99,10 @@ EXPORTS = {
     "pkv_block_refcount": (_i32, [_vp, _i32]),
     "pkv_seq_context_len": (_i64, [_vp, _i64]),
     "pkv_seq_num_blocks": (_i32, [_vp, _i64]),
+    "pkv_shared_prefix_members": (_i32, [_vp, _P(_i64), _i32, _i32, _P(_i32), _P(_i32), _P(_i32)]),
+    "pkv_blocks_for_budget": (_i32, [_sz, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_validate_decode_inputs": (_i32, [_P(_i32), _i32, _i32, _P(_i32), _P(_i32), _i32, _i32,
+                                          _i32, _P(_i32), _P(_i32), _i32, _i32]),
 }
 
 
@@ -449,6 +454,58 @@ def swap_blocks(k_cache, v_cache, k_host, v_host, pairs, direction: int, stream=
                                int(direction), _stream_ptr(stream)), "swap_blocks")
 
 
+# ------------------------------------------------------------------ host checks
+def blocks_for_budget(nbytes: int, num_layers: int, block_size: int, num_kv_heads: int,
+                      head_dim: int, dtype: int = BF16) -> int:
+    """Cache blocks (K and V of every layer) that ``nbytes`` of memory hold;
+    -1 for invalid sizes."""
+    return int(lib.pkv_blocks_for_budget(int(nbytes), num_layers, block_size, num_kv_heads,
+                                         head_dim, dtype))
+
+
+def _host_i32(a, what: str):
+    """A contiguous host int32 copy of ``a`` (numpy or torch) and its pointer."""
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def validate_decode_inputs(block_tables, context_lens, max_context_len: int, block_size: int,
+                           num_blocks: int, seq_order=None, members=None, member_flag=None,
+                           prefix_tokens: int = 0) -> None:
+    """Debug check of a decode call's index arrays on the host: every table
+    entry a context reads lies in the pool, every length within
+    ``max_context_len`` and the table width, the launch order is a
+    permutation, and shared-prefix members share their first
+    ``prefix_tokens`` tokens' blocks.  Raises ``PkvError`` (INVALID_ARG)
+    naming the first bad entry.  Device tensors are copied to the host."""
+    tb, tp = _host_i32(block_tables, "block_tables")
+    if tb.ndim != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    cx, cp = _host_i32(context_lens, "context_lens")
+    if cx.shape != (tb.shape[0],):
+        raise ValueError("context_lens must have one entry per table row")
+    keep = [tb, cx]
+    op = mp = fp = None
+    if seq_order is not None:
+        o, op = _host_i32(seq_order, "seq_order")
+        if o.shape != cx.shape:
+            raise ValueError("seq_order must have one entry per sequence")
+        keep.append(o)
+    nm = 0
+    if members is not None:
+        m, mp = _host_i32(members, "members")
+        f, fp = _host_i32(member_flag, "member_flag")
+        if f.shape != cx.shape:
+            raise ValueError("member_flag must have one entry per sequence")
+        keep += [m, f]
+        nm = m.size
+    _check(lib.pkv_validate_decode_inputs(tp, tb.shape[0], tb.shape[1], cp, op,
+                                          int(max_context_len), block_size, num_blocks, mp, fp,
+                                          nm, int(prefix_tokens)), "validate_decode_inputs")
+
+
 # ------------------------------------------------------------------ allocator
 class Allocator:
     """Host block allocator (C++); see ``pkv_allocator_*`` in ``include/pkv.h``."""
@@ -617,6 +674,23 @@ class Allocator:
             order_out.ctypes.data_as(po) if order_out is not None else None),
             "decode_step_prepare")
         return int(mx.value)
+
+    def shared_prefix_members(self, seqs: Sequence[int],
+                              prefix_tokens: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Batch positions of the sequences of ``seqs`` that share the blocks
+        of a ``prefix_tokens``-token prefix (the largest such group), and the
+        per-position flag: the ``members`` / ``member_flag`` arguments of
+        ``paged_attention_decode_shared_prefix``, int32."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        members = np.empty(max(len(s), 1), dtype=np.int32)
+        flag = np.empty(max(len(s), 1), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        po = ctypes.POINTER(ctypes.c_int32)
+        _check(lib.pkv_shared_prefix_members(self._h, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                             len(s), int(prefix_tokens), members.ctypes.data_as(po),
+                                             flag.ctypes.data_as(po), ctypes.byref(n)),
+               "shared_prefix_members")
+        return members[: n.value].copy(), flag[: len(s)].copy()
 
     def num_free_blocks(self) -> int:
         return int(lib.pkv_num_free_blocks(self._h))

@@ -664,3 +664,69 @@ extern "C" pkv_status pkv_longest_first_order(const int32_t* context_lens, int32
                    [&](int32_t x, int32_t y) { return context_lens[x] > context_lens[y]; });
   return pkv::ok();
 }
+
+// Sequences of a batch that share a prefix: those whose first
+// prefix_tokens / block_size blocks are the same physical blocks ("What Is
+// vLLM …", section "How does PagedAttention work?", memory-sharing step), with
+// at least one private token after it.  Sequences are grouped by that list
+// of blocks; the largest group (of at least two) is reported, the one met
+// first in seq_ids order on a tie.
+extern "C" pkv_status pkv_shared_prefix_members(const pkv_allocator* a, const int64_t* seq_ids,
+                                                int32_t num_seqs, int32_t prefix_tokens,
+                                                int32_t* members_out, int32_t* member_flag_out,
+                                                int32_t* num_members_out) {
+  const char* fn = "shared_prefix_members";
+  if (!a || num_seqs < 0 || !num_members_out ||
+      (num_seqs > 0 && (!seq_ids || !members_out || !member_flag_out)))
+    return fail(PKV_ERR_INVALID_ARG, "%s: bad arguments", fn);
+  if (prefix_tokens <= 0 || prefix_tokens % a->block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG, "%s: prefix_tokens=%d must be a positive multiple of %d",
+                fn, prefix_tokens, a->block_size);
+  std::unordered_set<int64_t> seen;
+  std::vector<const pkv_allocator::Seq*> seq(static_cast<size_t>(num_seqs), nullptr);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PKV_ERR_NOT_FOUND, "%s: unknown sequence %lld", fn, (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_SWAPPED, "%s: sequence %lld is swapped out", fn,
+                  (long long)seq_ids[i]);
+    if (!seen.insert(seq_ids[i]).second)
+      return fail(PKV_ERR_INVALID_ARG, "%s: sequence %lld listed twice", fn,
+                  (long long)seq_ids[i]);
+    seq[size_t(i)] = &it->second;
+  }
+  const size_t pb = size_t(prefix_tokens / a->block_size);
+  // group id of each eligible sequence: the index of the first sequence
+  // with the same prefix blocks
+  std::vector<int32_t> group(size_t(num_seqs), -1);
+  std::vector<int32_t> count(size_t(num_seqs), 0);
+  std::vector<int32_t> heads;  // first sequence of each group, in order
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const auto& s = *seq[size_t(i)];
+    if (s.len <= prefix_tokens) continue;
+    for (int32_t h : heads) {
+      const auto& t = *seq[size_t(h)];
+      if (std::equal(s.blocks.begin(), s.blocks.begin() + std::ptrdiff_t(pb), t.blocks.begin())) {
+        group[size_t(i)] = h;
+        break;
+      }
+    }
+    if (group[size_t(i)] < 0) {
+      group[size_t(i)] = i;
+      heads.push_back(i);
+    }
+    ++count[size_t(group[size_t(i)])];
+  }
+  int32_t best = -1;
+  for (int32_t h : heads)
+    if (count[size_t(h)] >= 2 && (best < 0 || count[size_t(h)] > count[size_t(best)])) best = h;
+  int32_t n = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const bool m = best >= 0 && group[size_t(i)] == best;
+    member_flag_out[i] = m ? 1 : 0;
+    if (m) members_out[n++] = i;
+  }
+  *num_members_out = n;
+  return pkv::ok();
+}

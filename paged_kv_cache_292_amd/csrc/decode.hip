@@ -953,10 +953,14 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
                                              int32_t block_size, int32_t max_context_len,
                                              int32_t partition_size, pkv_dtype dtype) {
   (void)block_size;
+  (void)num_kv_heads;
+  (void)dtype;
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  // AUTO: sized for the finest automatic partitioning of any kernel (the
+  // vector kernel's 4-heads layout partitions more coarsely or not at all),
+  // so the size does not depend on which kernel the call will take
   return pkv::workspace_for(num_seqs, num_q_heads, head_dim, max_context_len,
-                            pkv::decode_partition(dtype == PKV_BF16, num_q_heads, num_kv_heads,
-                                                  max_context_len, partition_size));
+                            pkv::resolve_partition(max_context_len, partition_size));
 }
 
 namespace {

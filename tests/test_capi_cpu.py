@@ -233,12 +233,32 @@ def test_decode_auto_partition_follows_the_kernel():
     assert P.decode_partition_size(8, 32, 8, 128, 16, 4000, P.PARTITION_AUTO, P.BF16) == 2048
     assert P.decode_partition_size(8, 4, 4, 64, 16, 4000, P.PARTITION_AUTO, P.F32) == 2048
     assert P.decode_partition_size(8, 4, 4, 64, 16, 2048, P.PARTITION_AUTO, P.F32) == 0
-    assert P.decode_workspace_bytes(128, 40, 40, 128, 16, 4150, P.PARTITION_AUTO, P.BF16) == 0
     P.set_decode_path(P.PATH_MFMA)
     try:  # forced onto the matrix cores: that kernel's rule
         assert P.decode_partition_size(128, 80, 40, 128, 16, 4150, P.PARTITION_AUTO, P.BF16) == 2048
     finally:
         P.set_decode_path(P.PATH_AUTO)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,bs,mx,dt", [
+    (128, 40, 40, 128, 16, 4150, 1), (128, 40, 40, 128, 16, 9000, 1), (64, 32, 32, 128, 16, 2048, 1),
+    (256, 32, 8, 128, 32, 8192, 1), (32, 64, 8, 128, 16, 32768, 1), (4, 4, 4, 64, 16, 3000, 0),
+])
+def test_auto_workspace_does_not_depend_on_the_decode_path(B, Hq, Hkv, D, bs, mx, dt):
+    """The AUTO workspace size is the same under every decode-path setting
+    and covers the partitions each path then uses."""
+    sizes = []
+    for path in (P.PATH_AUTO, P.PATH_VALU, P.PATH_MFMA):
+        P.set_decode_path(path)
+        try:
+            ws = P.decode_workspace_bytes(B, Hq, Hkv, D, bs, mx, P.PARTITION_AUTO, dt)
+            part = P.decode_partition_size(B, Hq, Hkv, D, bs, mx, P.PARTITION_AUTO, dt)
+        finally:
+            P.set_decode_path(P.PATH_AUTO)
+        need = 0 if part == 0 else B * Hq * (-(-mx // part)) * (D + 2) * 4
+        assert ws >= need, (path, part)
+        sizes.append(ws)
+    assert len(set(sizes)) == 1
 
 
 def test_prefill_partition_query():

@@ -50,6 +50,7 @@ class BenchStep:
     ctx: np.ndarray
     order: np.ndarray
     slots: np.ndarray        # the step's new slots (empty without new tokens)
+    members: np.ndarray      # shared-prefix members from the product allocator
     k_before: np.ndarray     # host caches before the step's cache write
     v_before: np.ndarray
     k_after: np.ndarray      # oracle caches after it
@@ -85,6 +86,11 @@ def bench_first_step(idx: int) -> BenchStep:
         tables_p, ctx_p = p.build_block_tables(seqs, max_blocks, pad=-1)
         order_p = P.longest_first_order(ctx_p)
         mx = int(ctx_p.max())
+    members = np.zeros(0, np.int32)
+    if s.num_sharers:  # as bench.py --shared-prefix takes them: from the tables
+        members, _ = p.shared_prefix_members(seqs, s.shared_prefix_tokens)
+        assert np.array_equal(members, wl.sharers)
+        assert list(members) == o.shared_prefix_members(list(range(B)), s.shared_prefix_tokens)
     p.close()
     tables_o, ctx_o = o.build_block_tables(list(range(B)), max_blocks, pad=-1)
     assert np.array_equal(slots_o, slots_p), "slots differ from the oracle allocator's"
@@ -103,7 +109,7 @@ def bench_first_step(idx: int) -> BenchStep:
         ka, va = OC.reshape_and_cache(wl.new_k, wl.new_v, kc, vc, slots_o)
     else:
         ka, va = kc, vc
-    return BenchStep(s, wl, tables_o, ctx_o, order_p, slots_o, kc, vc, ka, va)
+    return BenchStep(s, wl, tables_o, ctx_o, order_p, slots_o, members, kc, vc, ka, va)
 
 
 class Dev:
@@ -194,8 +200,8 @@ def test_full_gqa_prefix():
     d = Dev(st, write=False)
     assert_close(_decode(st, d, P.PARTITION_AUTO), ref, s.dtype, f"{s.name} full, AUTO")
     flag = np.zeros(s.num_seqs, dtype=np.int32)
-    flag[st.wl.sharers] = 1
-    members = torch.from_numpy(st.wl.sharers.astype(np.int32)).cuda()
+    flag[st.members] = 1
+    members = torch.from_numpy(st.members).cuda()
     out = torch.empty_like(d.q)
     P.paged_attention_decode_shared_prefix(out, d.q, d.k, d.v, d.tables, d.ctx, d.max_ctx,
                                            s.scale, members, torch.from_numpy(flag).cuda(),
