@@ -216,6 +216,35 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q,
                                       size_t workspace_bytes, pkv_dtype dtype,
                                       void* stream);
 
+/* Decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): pkv_paged_attention_decode with the
+ * split-K partials kept in a static device array of
+ * PKV_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  The call itself allocates and frees nothing.
+ * Arguments, results and errors as pkv_paged_attention_decode; a call whose
+ * partitions need more than PKV_NOALLOC_SCRATCH_BYTES (partition_size and
+ * pkv_decode_workspace_bytes tell the need) is refused with
+ * PKV_ERR_WORKSPACE before any launch.  The array's address on a device is
+ * looked up on the first call with that device current; `stream` must
+ * belong to the current device.  Every call on one GPU shares its array:
+ * calls that overlap on one GPU (concurrent streams, or host threads on
+ * different streams) race and give wrong results; calls in one stream are
+ * ordered and safe.  Nothing in the array needs to start at any value. */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q,
+                                              const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens,
+                                              const int32_t* seq_order,
+                                              int32_t max_context_len, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, float scale,
+                                              int32_t partition_size, pkv_dtype dtype,
+                                              void* stream);
+
 /* Paged decode for a batch in which some sequences share a prefix ("What Is
  * vLLM …", section "How does PagedAttention work?", the memory-sharing
  * step: sequences that share a prefix point at the same physical blocks).

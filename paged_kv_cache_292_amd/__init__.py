@@ -24,7 +24,8 @@ __all__ = [
     "paged_attention_prefill", "prefill_workspace_bytes", "prefill_partition_size",
     "swap_blocks", "SWAP_OUT", "SWAP_IN",
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
-    "blocks_for_budget", "validate_decode_inputs",
+    "blocks_for_budget", "validate_decode_inputs", "paged_attention_decode_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
@@ -33,6 +34,7 @@ LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
 F32 = 0
 BF16 = 1
 PARTITION_AUTO = -1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 
 STATUS = {
@@ -55,6 +57,9 @@ EXPORTS = {
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                           _i32, _vp]),
+    "pkv_paged_attention_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                                  _i32, _vp]),
     "pkv_paged_attention_decode_shared_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                                         _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                         _f32, _vp, _vp, _i32, _i32, _vp, _sz,
@@ -319,6 +324,25 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         op, qp, k_cache.data_ptr(), v_cache.data_ptr(), idx[0], block_tables.shape[1], idx[1],
         idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
         ws_ptr, ws_bytes, dt, _stream_ptr(stream)), fn)
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   max_context_len: int, scale: float,
+                                   partition_size: int = PARTITION_AUTO, stream=None,
+                                   seq_order=None) -> None:
+    """``paged_attention_decode`` with no workspace argument: the library's
+    static per-GPU scratch array (``NOALLOC_SCRATCH_BYTES``) holds the
+    partials, so the call allocates nothing.  Calls that overlap on one GPU
+    race on that array."""
+    fn = "paged_attention_decode_noalloc"
+    B, Hq = q.shape[0], q.shape[1]
+    idx = _decode_indices(block_tables, context_lens, seq_order, B, fn)
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
+    qp, op = _q_out(q, out, (B, Hq, D), k_cache.dtype, fn)
+    _check(lib.pkv_paged_attention_decode_noalloc(
+        op, qp, k_cache.data_ptr(), v_cache.data_ptr(), idx[0], block_tables.shape[1], idx[1],
+        idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), int(partition_size),
+        dt, _stream_ptr(stream)), fn)
 
 
 def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens,

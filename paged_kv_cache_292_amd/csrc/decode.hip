@@ -25,6 +25,8 @@
 //
 // Chunked prefill (several queries per sequence) shares the argument block
 // and helpers in attn_common.h and lives in prefill.hip.
+#include <mutex>
+
 #include "attn_common.h"
 
 namespace pkv {
@@ -1174,4 +1176,60 @@ extern "C" pkv_status pkv_paged_attention_decode_write(
                      max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                      partition_size, workspace, workspace_bytes, dtype, stream, &w);
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate (code
+// under graph capture, tight serving loops): the split-K partials live in a
+// static device array of PKV_NOALLOC_SCRATCH_BYTES, one per GPU for the life
+// of the process.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in); it looks up the array's device address
+// once per device, with that device current, and passes that.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+pkv_status scratch_of_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_HIP, "%s: no current device (%s)", fn, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PKV_ERR_HIP, "%s: device address of the scratch array on device %d: %s", fn,
+                  dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return pkv::ok();
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attention_decode_noalloc(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_size, pkv_dtype dtype, void* stream) {
+  const char* fn = "paged_attention_decode_noalloc";
+  void* ws = nullptr;
+  const pkv_status st = scratch_of_current_device(fn, &ws);
+  if (st != PKV_OK) return st;
+  // the same checks and launches as pkv_paged_attention_decode, with the
+  // scratch array as a workspace of its fixed size (a larger need is
+  // refused with PKV_ERR_WORKSPACE before any launch)
+  return decode_call(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, seq_order, max_context_len, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size, ws,
+                     size_t(PKV_NOALLOC_SCRATCH_BYTES), dtype, stream, nullptr);
 }
