@@ -594,10 +594,11 @@ def main() -> int:
         if fused_write:  # the new rows read from the input and written into the cache
             other += 2 * 2 * B * Hkv * D * E
         if part_used > 0:
-            if shared:  # the prefix, then partitions of max(2048, prefix) tokens
-                F = s.shared_prefix_tokens
+            if shared:  # members: the prefix, then partitions of max(2048, prefix)
+                F = s.shared_prefix_tokens  # tokens; the others: max(2048, prefix)
                 Pp = max(2048, F)
-                np_ = np.where(ctx > F, 1 + (ctx - F + Pp - 1) // Pp, 1)
+                np_ = np.where(flag != 0, np.where(ctx > F, 1 + (ctx - F + Pp - 1) // Pp, 1),
+                               (ctx + Pp - 1) // Pp)
             else:
                 np_ = (ctx + part_used - 1) // part_used
             multi = np_[np_ > 1].sum()

@@ -249,14 +249,18 @@ pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q,
  * vLLM …", section "How does PagedAttention work?", the memory-sharing
  * step: sequences that share a prefix point at the same physical blocks).
  * The result is that of pkv_paged_attention_decode (equal up to rounding):
- * contexts are split into a first partition of prefix_tokens tokens and
- * then partitions of max(2048, prefix_tokens) tokens, merged by
+ * a member's context is split into a first partition of prefix_tokens
+ * tokens and then partitions of max(2048, prefix_tokens) tokens, every other
+ * context into partitions of max(2048, prefix_tokens) tokens, all merged by
  * log-sum-exp.  Partition 0 of every member, the shared prefix, is computed
  * once for tiles of 16 / G members (G = num_q_heads / num_kv_heads): each
- * K/V row of the prefix is read once per tile instead of once per member,
- * and the tiles run in the same launch as the other partitions.  With
- * num_members = 0 the call is pkv_paged_attention_decode with
- * partition_size = prefix_tokens.
+ * K/V row of the prefix is read once per tile instead of once per member.
+ * The tiles run first in the same launch as the other partitions, all tiles
+ * of one kv head on one XCD (with the kv heads in eights), so that the
+ * prefix comes from HBM about once per kv head.  With num_members = 0 the
+ * call is pkv_paged_attention_decode with partition_size = prefix_tokens.
+ * pkv_shared_prefix_members derives members and member_flag from the
+ * allocator's tables, and pkv_validate_decode_inputs checks them.
  * members       device int32 [num_members]: the sharing sequences (distinct
  *               indices into the batch).  Each member's first
  *               prefix_tokens / block_size table entries must be the same

@@ -39,6 +39,7 @@ struct AttnArgs {
   const int32_t* order;  // optional launch order of the sequences (a permutation)
   const int32_t* query_start;  // prefill: first query row of each sequence [B + 1]
   int32_t q_tiles;             // prefill: query tiles per sequence (grid y = kv heads x tiles)
+  int32_t q_groups;            // prefill: workgroups of query tiles per (sequence, kv head)
   int32_t total_queries;       // prefill: rows of q / out
   float* part_o;   // [B, Hq, max_parts, D]
   float* part_ml;  // [B, Hq, max_parts, 2] (max in log2 units, sum)
@@ -57,8 +58,10 @@ struct AttnArgs {
   const int32_t* members;
   const int32_t* member_flag;
   int32_t num_members;
-  int32_t group_z0;
-  int32_t first_part;  // > 0: partition 0 is this many tokens, the rest `partition` each
+  int32_t group_z0;    // first grid row of the shared-prefix tiles
+  int32_t group_z1;    // one past their last row
+  int32_t seq_z0;      // first grid row of the sequences
+  int32_t first_part;  // > 0: a member's partition 0 is this many tokens, the rest `partition` each
   float scale_log2;   // scale * log2(e): logits are kept in base-2 units
 };
 
@@ -83,18 +86,24 @@ __device__ __forceinline__ void query_range(const AttnArgs& a, int b, int& first
 }
 
 // Token range [start, start + length) of partition p and the number of
-// partitions of a ctx-token context (uniform unless first_part > 0).
-__device__ __forceinline__ int part_begin(const AttnArgs& a, int p) {
-  return a.first_part > 0 ? (p == 0 ? 0 : a.first_part + (p - 1) * a.partition)
-                          : p * a.partition;
+// partitions of a ctx-token context: uniform partitions of a.partition
+// tokens, or (fp > 0) a first partition of fp tokens and then uniform ones.
+__device__ __forceinline__ int part_begin(const AttnArgs& a, int fp, int p) {
+  return fp > 0 ? (p == 0 ? 0 : fp + (p - 1) * a.partition) : p * a.partition;
 }
-__device__ __forceinline__ int part_length(const AttnArgs& a, int p) {
-  return a.first_part > 0 && p == 0 ? a.first_part : a.partition;
+__device__ __forceinline__ int part_length(const AttnArgs& a, int fp, int p) {
+  return fp > 0 && p == 0 ? fp : a.partition;
 }
-__device__ __forceinline__ int part_count(const AttnArgs& a, int ctx) {
-  if (a.first_part > 0)
-    return ctx <= a.first_part ? 1 : 1 + (ctx - a.first_part + a.partition - 1) / a.partition;
+__device__ __forceinline__ int part_count(const AttnArgs& a, int fp, int ctx) {
+  if (fp > 0) return ctx <= fp ? 1 : 1 + (ctx - fp + a.partition - 1) / a.partition;
   return (ctx + a.partition - 1) / a.partition;
+}
+
+// First-partition length of sequence b: in a shared-prefix call, the prefix
+// for the sharing sequences (their partition 0 is computed once per tile);
+// every other sequence keeps uniform partitions.
+__device__ __forceinline__ int first_part_of(const AttnArgs& a, int b) {
+  return a.first_part > 0 && a.member_flag[b] != 0 ? a.first_part : 0;
 }
 
 __device__ __forceinline__ int clamp_ctx(const AttnArgs& a, int b) {
@@ -110,6 +119,14 @@ typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyMax = 8.0f;  // log2 of the largest p allowed before rescaling
+
+// Maximum of two scores (never NaN: finite or -inf).  The IEEE 754-2019
+// maximum lowers to v_maximum3_f32 with no quieting of its inputs, where
+// fmaxf canonicalises any input the compiler cannot prove canonical (one
+// extra instruction per score where masked and unmasked scores merge).
+__device__ __forceinline__ float vmax(float x, float y) {
+  return __builtin_elementwise_maximum(x, y);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2v_t v = {lo, hi};

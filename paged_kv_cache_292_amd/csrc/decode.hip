@@ -413,9 +413,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane >> 4;
   const int n = lane & 15;
-  const int kvh0 = blockIdx.y * HG;  // first kv head of the workgroup
-  const int kvh = kvh0 + wave % HG;  // this wave's kv head
-  const int stream = wave / HG;      // this wave's chunk stream
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
@@ -423,9 +420,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   // Shared-prefix rows: a tile of 16 / G members sharing the prefix; its
   // operand columns are (member, query head) pairs, and it computes the
   // members' partition 0 (the prefix) with one read of the prefix's K/V.
-  const bool group = !WRITE && a.members != nullptr && int(blockIdx.z) >= a.group_z0;
+  // Grid rows: the sequences' rows from seq_z0, the tiles' rows from
+  // group_z0 to group_z1.
+  const bool group = !WRITE && a.members != nullptr && int(blockIdx.z) >= a.group_z0 &&
+                     int(blockIdx.z) < a.group_z1;
+  // The tiles' workgroups in launch order: workgroup w takes kv head
+  // w % Hkv and tile w / Hkv, so with the kv heads in eights every tile of a
+  // kv head lands on the same XCD (workgroups are dealt to the 8 XCDs
+  // round-robin) and reads the prefix rows the others fetched into its L2.
+  const int gw = group ? int(blockIdx.x) + int(gridDim.x) * (int(blockIdx.y) +
+                                                             int(gridDim.y) * (int(blockIdx.z) - a.group_z0))
+                       : 0;
+  const int kvh0 = group ? gw % Hkv : int(blockIdx.y) * HG;  // first kv head
+  const int kvh = kvh0 + wave % HG;  // this wave's kv head
+  const int stream = wave / HG;      // this wave's chunk stream
   const int mpg = 16 / G;  // members per tile
-  const int tile = group ? (int(blockIdx.z) - a.group_z0) * int(gridDim.x) + int(blockIdx.x) : 0;
+  const int tile = group ? gw / Hkv : 0;
   const int tile_members = group ? min(mpg, a.num_members - tile * mpg) : 0;
   if (group && tile_members <= 0) return;
   auto member_seq = [&](int i) {
@@ -433,14 +443,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
     return (unsigned)s < (unsigned)a.num_seqs ? s : 0;
   };
   const int part = group ? 0 : int(blockIdx.x);
-  const int b = group ? member_seq(tile * mpg) : seq_of(a, blockIdx.z);
+  const int b = group ? member_seq(tile * mpg) : seq_of(a, int(blockIdx.z) - a.seq_z0);
 
   // The 16 operand columns are the G query heads of this kv head (padded
   // with zero columns); the query sees the sequence's whole context.
-  const int ctx = group ? min(part_length(a, 0), a.ctx_cap) : clamp_ctx(a, b);
-  const int t0 = part_begin(a, part);
-  const int t1 = min(ctx, t0 + part_length(a, part));
-  const int nparts = group ? 2 : part_count(a, ctx);  // group: partials
+  const int fp = group ? a.first_part : first_part_of(a, b);
+  const int ctx = group ? min(a.first_part, a.ctx_cap) : clamp_ctx(a, b);
+  const int t0 = part_begin(a, fp, part);
+  const int t1 = min(ctx, t0 + part_length(a, fp, part));
+  const int nparts = group ? 2 : part_count(a, fp, ctx);  // group: partials
   if (!group && a.member_flag != nullptr && part == 0 && nparts >= 2 && a.member_flag[b] != 0)
     return;  // the shared-prefix rows compute this partition
   const int rows = group ? tile_members * G : G;  // valid operand columns
@@ -729,7 +740,7 @@ __global__ __launch_bounds__(64) void reduce_partitions_kernel(AttnArgs a) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int ctx = clamp_ctx(a, b);
-  const int nparts = part_count(a, ctx);
+  const int nparts = part_count(a, first_part_of(a, b), ctx);
   if (nparts <= 1) return;  // written directly by the partition kernel
   const size_t head = size_t(b) * a.num_q_heads + h;
   const float* ml = a.part_ml + 2 * head * a.max_parts;
@@ -830,13 +841,21 @@ hipError_t launch_mfma(const AttnArgs& a, const NewRows& w, int num_seqs, hipStr
                        dim3(kMfmaNW * 64), 0, st, a, w);
   } else {
     dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
+    AttnArgs ag = a;
     if (!WRITE && a.members != nullptr && a.num_members > 0) {
-      // shared-prefix tiles after the sequences' rows, grid.x tiles per row
+      // shared-prefix tiles: grid.x * num_kv_heads workgroups per row, in
+      // the rows before the sequences' (measured on MI355X, GQA batch with
+      // 128 of 256 sequences sharing 1,024 tokens: 663 us against 666 us with
+      // the tiles after the sequences)
       const int mpg = 16 / (a.num_q_heads / a.num_kv_heads);
       const int tiles = (a.num_members + mpg - 1) / mpg;
-      grid.z += unsigned((tiles + int(grid.x) - 1) / int(grid.x));
+      const int rows = (tiles + int(grid.x) - 1) / int(grid.x);
+      ag.group_z0 = 0;  // first: the tiles read the prefix while the rest starts
+      ag.group_z1 = rows;
+      ag.seq_z0 = rows;
+      grid.z += unsigned(rows);
     }
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW, 1, WRITE>), grid, dim3(kNW * 64), 0, st, a,
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW, 1, WRITE>), grid, dim3(kNW * 64), 0, st, ag,
                        w);
   }
   return hipGetLastError();
@@ -1015,8 +1034,10 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL pointer argument", fn);
 
-  // Shared prefix: partition 0 is the prefix (first_part tokens), the rest
-  // partitions of the shared-prefix length rule (at least the prefix).
+  // Shared prefix: a member's partition 0 is the prefix (first_part tokens),
+  // its later partitions and every other sequence's partitions are of the
+  // shared-prefix length rule (max(2048, prefix) tokens); the workspace and
+  // the grid are sized for the members' scheme, which has the most.
   const int32_t first_part = num_members > 0 ? partition_size : 0;
   const int32_t partition =
       first_part > 0 ? pkv::shared_partition(max_context_len, first_part)
@@ -1041,6 +1062,8 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
   a.member_flag = num_members > 0 ? member_flag : nullptr;
   a.num_members = num_members;
   a.group_z0 = num_seqs;
+  a.group_z1 = 1 << 30;
+  a.seq_z0 = 0;
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.ctx_cap = cap;

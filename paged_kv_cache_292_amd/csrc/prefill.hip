@@ -37,15 +37,40 @@ namespace {
 // columns of the matrix products (the decode kernel's layout, with queries
 // added), and each wave owns TPW consecutive tiles.  Each K/V chunk (64
 // tokens for 8-wave workgroups, 32 for 4-wave ones) is loaded once by the
-// whole workgroup — whole rows, streamed — into a double-buffered LDS tile,
+// whole workgroup — whole rows, cached in L2 for the kv head's other
+// workgroups (placed on the same XCD) — into a double-buffered LDS tile,
 // one barrier per chunk; every wave reads each K and V operand from LDS once
 // and uses it for all of its tiles (LDS reads per flop fall with TPW).  The
 // products run over the chunk in 32-token passes, both on 32-deep matrix
 // instructions: q.K^T over head_dim, and P.V over the pass's 32 tokens, its
-// V operand read transposed from LDS.
+// V operand read transposed from LDS.  The q.K^T products of one k step are
+// issued together (2 * TPW independent chains); the softmax keeps its running
+// maximum from the raw products and applies the scale inside the exponent
+// (p = 2^(s * |scale| - m), one fma per score).
 // The next chunks' loads are in flight while the current one is computed.
 // Tiles that see no token of a chunk (the causal boundary) skip its math;
 // their waves keep to the barriers.
+// Grid row y -> (kv head, query-tile group).  With the kv heads in eights,
+// the groups of one kv head sit 8 workgroups apart: the dispatcher deals
+// workgroups to the 8 XCDs round-robin, so they land on one XCD back to back,
+// stream the same K/V rows at about the same time and the later ones find
+// them in that XCD's L2 (measured on MI355X, 16 sequences x 40 heads x
+// 512-token chunks, two groups per kv head: HBM reads 1.46x the K/V bytes
+// with the groups 40 workgroups apart and non-temporal loads, 0.98x paired
+// with cached loads, and 5% faster).
+__device__ __forceinline__ void prefill_group_of(const AttnArgs& a, int y, int& kvh, int& grp) {
+  if (a.num_kv_heads % 8 == 0) {
+    const int groups = a.q_groups;
+    const int blk = y / (8 * groups);  // block of 8 kv heads
+    const int r = y % (8 * groups);
+    kvh = blk * 8 + r % 8;
+    grp = r / 8;
+  } else {
+    kvh = y % a.num_kv_heads;
+    grp = y / a.num_kv_heads;
+  }
+}
+
 template <int D, int BS, int NWP, int TPW>
 __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 32;
@@ -75,8 +100,11 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   const int c = lane >> 4;
   const int n = lane & 15;
   const int part = blockIdx.x;
-  const int kvh = int(blockIdx.y) % a.num_kv_heads;
-  const int tile0 = ((int(blockIdx.y) / a.num_kv_heads) * NWP + wave) * TPW;  // first own tile
+  int kvh_, grp_;
+  prefill_group_of(a, int(blockIdx.y), kvh_, grp_);
+  const int kvh = kvh_;
+  const int grp = grp_;
+  const int tile0 = (grp * NWP + wave) * TPW;  // first own tile
   const int b = seq_of(a, blockIdx.z);
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
@@ -87,7 +115,7 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
   int qrow0, nq;
   query_range(a, b, qrow0, nq);
   // workgroup-wide token range: the causal end of its last tile with queries
-  const int g_first = (int(blockIdx.y) / a.num_kv_heads) * NWP * TPW * QPT;
+  const int g_first = grp * NWP * TPW * QPT;
   if (g_first >= nq) return;  // uniform over the workgroup
   const int g_last = min(g_first + NWP * TPW * QPT, nq) - 1;
   const int t0 = part * a.partition;
@@ -127,6 +155,13 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
     return;
   }
 
+  // logits = scale * (q . k): with a negative scale the q operand is negated
+  // (exact in bf16) and |scale| used, so that the largest product is the
+  // largest logit; a zero scale becomes the smallest normal float, which
+  // leaves every weight 2^0 = 1 as it should
+  const bool neg_scale = a.scale_log2 < 0.0f;
+  const float sp = neg_scale ? -a.scale_log2 : (a.scale_log2 > 0.0f ? a.scale_log2 : FLT_MIN);
+  const uint32_t qsign = neg_scale ? 0x80008000u : 0u;
   uint4 qop[TPW][KSTEPS];
   f32x4_t acc[TPW][EPL];
   float m[TPW], l[TPW];
@@ -136,8 +171,12 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
         static_cast<const uint16_t*>(a.q) + out_row(u, row_ok[u] ? n : 0) * D + 8 * c;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
-      const uint4 v = row_ok[u] ? *reinterpret_cast<const uint4*>(qh + 32 * j)
-                                : make_uint4(0u, 0u, 0u, 0u);
+      uint4 v = row_ok[u] ? *reinterpret_cast<const uint4*>(qh + 32 * j)
+                          : make_uint4(0u, 0u, 0u, 0u);
+      v.x ^= qsign;
+      v.y ^= qsign;
+      v.z ^= qsign;
+      v.w ^= qsign;
       qop[u][j] = v;
     }
 #pragma unroll
@@ -198,7 +237,9 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
       const bool in = tc + ptok[k] < g_t1;
       const size_t b0 = NBC > 1 && in ? blk[ptok[k] / BS] : blk[0];
       const uint32_t off = !live ? 0u : (in ? poff[k] : poff0[k]);
-      stage[k] = load16<true>(pbase[k] + b0 + off);
+      // cached loads: the other query-tile groups of this kv head read the
+      // same rows from L2 shortly after
+      stage[k] = load16<false>(pbase[k] + b0 + off);
     }
   };
   auto store = [&](int buf, const Stage& stage) {
@@ -213,98 +254,117 @@ __global__ __launch_bounds__(NWP * 64) void prefill_lds_kernel(AttnArgs a) {
     }
   };
 
-  auto compute = [&](int ch, int buf) {
+  // S^T = K . Q^T for every tile and each 16-token half h of a 32-token pass,
+  // each K operand read once; the k step outermost, so the 2 * TPW products
+  // of one step are independent
+  auto qk = [&](const char* ks, f32x4_t (&s)[TPW][2]) {
 #pragma unroll
-    for (int sb = 0; sb < CH / SUB; ++sb) {
-      const int tc = ch * CH + sb * SUB;
-      if (tc >= t1_max) break;  // none of this wave's tiles sees a token from here on
-      const char* ks = s_k[buf] + sb * SUB * PITCH_K;
-      const char* vs = s_v[buf] + sb * SUB * PITCH_V;
-      // S^T = K . Q^T for every tile and each 16-token half h of the chunk,
-      // each K operand read once
-      f32x4_t s[TPW][2];
+    for (int u = 0; u < TPW; ++u) s[u][0] = s[u][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) s[u][0] = s[u][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < KSTEPS; ++j) {
+      bf16x8_t kop[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        kop[h] = __builtin_bit_cast(
+            bf16x8_t,
+            *reinterpret_cast<const uint4*>(ks + (16 * h + n) * PITCH_K + 16 * c + 64 * j));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) {
-          const bf16x8_t kop = __builtin_bit_cast(
-              bf16x8_t,
-              *reinterpret_cast<const uint4*>(ks + (16 * h + n) * PITCH_K + 16 * c + 64 * j));
+        for (int u = 0; u < TPW; ++u)
+          s[u][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kop[h], __builtin_bit_cast(bf16x8_t, qop[u][j]), s[u][h], 0, 0, 0);
+    }
+  };
+  // Tile u's scores of the pass at token tc: the raw products (masked: -inf)
+  // into sc, and the running maximum moved (with the rescale) where a score
+  // passed it by more than 2^kLazyMax.
+  auto scores = [&](int tc, int u, const f32x4_t (&su)[2], float (&sc)[8]) {
+    // sc[4h + i]: token tc + 16h + 4c + i of query row n
+    if (tc >= t0 && tc + SUB <= t1[u] && tc + SUB - 1 <= pos_lo[u]) {  // all visible
 #pragma unroll
-          for (int u = 0; u < TPW; ++u)
-            s[u][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                kop, __builtin_bit_cast(bf16x8_t, qop[u][j]), s[u][h], 0, 0, 0);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[4 * h + i] = su[h][i];
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tc + 16 * h + 4 * c + i;
+          sc[4 * h + i] = (t >= t0 && t < t1[u] && t <= pos_n[u]) ? su[h][i] : -INFINITY;
         }
+    }
+    const float mx = vmax(vmax(vmax(sc[0], sc[1]), vmax(sc[2], sc[3])),
+                          vmax(vmax(sc[4], sc[5]), vmax(sc[6], sc[7]))) * sp;
+    if (__ballot(mx > m[u] + kLazyMax)) {
+      float hm = fmaxf(mx, __shfl_xor(mx, 16));
+      hm = fmaxf(hm, __shfl_xor(hm, 32));
+      const float mn = hm > m[u] + kLazyMax ? hm : m[u];
+      const float alpha = fast_exp2(m[u] - mn);
+      l[u] *= alpha;
+#pragma unroll
+      for (int t = 0; t < EPL; ++t) acc[u][t] *= alpha;
+      m[u] = mn;
+    }
+  };
+  // The weights p = 2^(s |scale| - m) of tile u, added to its sum and packed
+  // to bf16 as the P^T operand.
+  auto weights = [&](int u, const float (&sc)[8]) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], sp, -m[u]));
+    l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    return __builtin_bit_cast(
+        bf16x8_t, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+  };
+  // O^T += V^T . P^T, tile by tile (one tile's V operand live at a time).
+  // The V^T operand of output tile t (dims 16t .. 16t+15) over the pass's 32
+  // tokens has k-slots 8c .. 8c+7 = tokens 4c .. 4c+3 and 16+4c .. 16+4c+3,
+  // the tokens whose scores lane (c, n) holds.  It comes straight from LDS
+  // with the transposing read: in each 16-lane group, lane k reads 8 bytes
+  // of row r0 + k/4 at dims 16t + 4(k%4), and lane j receives element j%4 of
+  // the reads of lanes j/4, j/4 + 4, + 8, + 12, i.e. dim 16t + j of rows
+  // r0 .. r0+3.
+  auto pv = [&](const char* vs, const bf16x8_t (&pb)[TPW]) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const char* vrow = vs + (4 * c + (n >> 2)) * PITCH_V + 8 * (n & 3);
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) {
+      const uint2 lo = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 32 * t)));
+      const uint2 hi = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 16 * PITCH_V + 32 * t)));
+      const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u], acc[u][t], 0, 0, 0);
+    }
+  };
+  constexpr int NP = CH / SUB;  // 32-token passes per chunk
+  const bf16x8_t pzero = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+
+  auto compute = [&](int ch, int buf) {
+#pragma unroll
+    for (int sb = 0; sb < NP; ++sb) {
+      const int tc = ch * CH + sb * SUB;
+      if (tc >= t1_max) break;  // none of this wave's tiles sees a token from here on
+      f32x4_t s[TPW][2];
+      qk(s_k[buf] + sb * SUB * PITCH_K, s);
       bf16x8_t pb[TPW];
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         if (tc >= t1[u]) {  // wave-uniform: the tile adds nothing (every V row in LDS is finite)
-          pb[u] = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+          pb[u] = pzero;
           continue;
         }
-        // sc[4h + i]: token tc + 16h + 4c + i of query row n
         float sc[8];
-        // every row sees every token of the pass
-        if (tc >= t0 && tc + SUB <= t1[u] && tc + SUB - 1 <= pos_lo[u]) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[4 * h + i] = s[u][h][i] * a.scale_log2;
-        } else {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = tc + 16 * h + 4 * c + i;
-              sc[4 * h + i] =
-                  (t >= t0 && t < t1[u] && t <= pos_n[u]) ? s[u][h][i] * a.scale_log2 : -INFINITY;
-            }
-        }
-        const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                               fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        if (__ballot(mx > m[u] + kLazyMax)) {
-          float hm = fmaxf(mx, __shfl_xor(mx, 16));
-          hm = fmaxf(hm, __shfl_xor(hm, 32));
-          const float mn = hm > m[u] + kLazyMax ? hm : m[u];
-          const float alpha = fast_exp2(m[u] - mn);
-          l[u] *= alpha;
-#pragma unroll
-          for (int t = 0; t < EPL; ++t) acc[u][t] *= alpha;
-          m[u] = mn;
-        }
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sc[i] - m[u]);
-        l[u] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        pb[u] = __builtin_bit_cast(
-            bf16x8_t, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+        scores(tc, u, s[u], sc);
+        pb[u] = weights(u, sc);
       }
-      // O^T += V^T . P^T, tile by tile (one tile's V operand live at a time).
-      // The V^T operand of output tile t (dims 16t .. 16t+15) over the chunk's
-      // 32 tokens has k-slots 8c .. 8c+7 = tokens 4c .. 4c+3 and 16+4c ..
-      // 16+4c+3, the tokens whose scores lane (c, n) holds.  It comes straight
-      // from LDS with the transposing read: in each 16-lane group, lane k reads
-      // 8 bytes of row r0 + k/4 at dims 16t + 4(k%4), and lane j receives
-      // element j%4 of the reads of lanes j/4, j/4 + 4, + 8, + 12, i.e. dim
-      // 16t + j of rows r0 .. r0+3.
-      typedef short v4s __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(3))) v4s* lds_v4s;
-      const char* vrow = vs + (4 * c + (n >> 2)) * PITCH_V + 8 * (n & 3);
-#pragma unroll
-      for (int t = 0; t < EPL; ++t) {
-        const uint2 lo = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 32 * t)));
-        const uint2 hi = __builtin_bit_cast(
-            uint2,
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vrow + 16 * PITCH_V + 32 * t)));
-        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-        for (int u = 0; u < TPW; ++u)
-          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pb[u], acc[u][t], 0, 0, 0);
-      }
+      pv(s_v[buf] + sb * SUB * PITCH_V, pb);
     }
   };
 
@@ -578,6 +638,10 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.order = seq_order;
   a.query_start = query_start;
   a.q_tiles = int32_t(tiles);
+  {
+    const int tpg = pkv::prefill_tiles_per_group(int(tiles));
+    a.q_groups = int32_t((tiles + tpg - 1) / tpg);
+  }
   a.total_queries = total_queries;
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
