@@ -11,6 +11,7 @@ import pytest
 import test_oracle_allocator as TAL
 import test_oracle_attention as TA
 import test_oracle_cache_write as TC
+import test_oracle_host_checks as THC
 import test_oracle_prefix_cache as TPC
 import test_oracle_swap as TS
 
@@ -177,3 +178,25 @@ PREFIX = [
 def test_prefix_cache_mutant_caught(old, new, monkeypatch):
     monkeypatch.setattr(TPC, "OAL", _mutant("oracle/allocator.py", old, new))
     assert _caught(TPC.PINS)
+
+
+MEMBERS = [
+    # sequences no longer than the prefix counted as members
+    ("            if self.lengths[s] > prefix_tokens:\n", "            if self.lengths[s] >= prefix_tokens:\n"),
+    # grouped by one block too few
+    ("groups.setdefault(tuple(self.tables[s][:nb]), []).append(i)",
+     "groups.setdefault(tuple(self.tables[s][:nb - 1]), []).append(i)"),
+    # a lone sequence reported as a group
+    ("if len(g) >= 2 and len(g) > len(best):", "if len(g) >= 1 and len(g) > len(best):"),
+    # the last group met wins a tie
+    ("if len(g) >= 2 and len(g) > len(best):", "if len(g) >= 2 and len(g) >= len(best):"),
+    # sequence ids instead of positions in the batch
+    ("groups.setdefault(tuple(self.tables[s][:nb]), []).append(i)",
+     "groups.setdefault(tuple(self.tables[s][:nb]), []).append(s)"),
+]
+
+
+@pytest.mark.parametrize("old,new", MEMBERS, ids=[f"members{i}" for i in range(len(MEMBERS))])
+def test_shared_prefix_members_mutant_caught(old, new, monkeypatch):
+    monkeypatch.setattr(THC, "OAL", _mutant("oracle/allocator.py", old, new))
+    assert _caught(THC.PINS)
