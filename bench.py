@@ -50,6 +50,10 @@ def _args():
     ap.add_argument("--serial-upload", action="store_true",
                     help="upload each step's tables on the compute stream instead of a side "
                          "stream overlapped with the previous step's attention")
+    ap.add_argument("--upload-kernel", action="store_true",
+                    help="decode steps with new tokens: upload each step's tables with their own "
+                         "upload launch (side stream, or --serial-upload) instead of within the "
+                         "previous step's decode launch (paged_attention_decode_step)")
     ap.add_argument("--staging-depth", type=int, default=8,
                     help="pinned staging buffers in flight (steps the host may run ahead)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
@@ -490,7 +494,13 @@ def main() -> int:
     step_new = 1 if s.new_tokens else 0
     chunk = s.chunk  # > 0: a chunked-prefill step of this many tokens per sequence
     step_tok = chunk if chunk else step_new  # tokens each sequence gains per step
-    wl = W.make_workload(s, extra_tokens=total_steps * step_tok)
+    # decode steps with new tokens write them inside the decode launch, and
+    # (unless --upload-kernel) that launch also uploads the next step's
+    # tables, which the host prepares one step ahead
+    fused_write = bool(step_new) and not s.chunk and not args.separate_write
+    in_step = fused_write and not args.upload_kernel and not args.serial_upload
+    # growth room: in_step prepares one step more than it decodes
+    wl = W.make_workload(s, extra_tokens=(total_steps + int(in_step)) * step_tok)
     B, Hq, Hkv, D, bs = s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size
     dt_code = P.F32 if s.dtype == "f32" else P.BF16
     tdt = torch.float32 if s.dtype == "f32" else torch.bfloat16
@@ -503,7 +513,7 @@ def main() -> int:
     alloc = P.Allocator(wl.num_blocks, bs, wl.free_order)
     alloc.replay(wl.ops)
     seqs = np.arange(B, dtype=np.int64)
-    final_ctx = wl.ctx + (total_steps - 1) * step_tok
+    final_ctx = wl.ctx + (total_steps - 1 + int(in_step)) * step_tok
     max_blocks = int(((final_ctx + bs - 1) // bs).max())
     max_ctx_final = int(final_ctx.max())
 
@@ -582,8 +592,6 @@ def main() -> int:
     E = s.elem_bytes
 
     qrows = chunk if chunk else 1  # query rows per sequence
-    # decode steps with new tokens write them inside the decode launch
-    fused_write = bool(step_new) and not chunk and not args.separate_write
 
     def decode_bytes(ctx):
         """Unique K/V bytes of the step's sequences, and those plus q, out,
@@ -593,6 +601,8 @@ def main() -> int:
         other = 2 * B * qrows * Hq * D * E + 4 * nb + 4 * B
         if fused_write:  # the new rows read from the input and written into the cache
             other += 2 * 2 * B * Hkv * D * E
+        if in_step:  # the next step's arrays written into device memory
+            other += stage_bytes
         if part_used > 0:
             if shared:  # members: the prefix, then partitions of max(2048, prefix)
                 F = s.shared_prefix_tokens  # tokens; the others: max(2048, prefix)
@@ -685,6 +695,50 @@ def main() -> int:
         ctx_hist.append(cx)
         host_s.append(time.perf_counter() - t_h)
 
+    # In-step upload: the host prepares step k's tables into pinned buffer
+    # k % nbuf before step k - 1 is launched; step k - 1's decode launch copies
+    # them into the device staging buffer that step k reads (the other one of
+    # two), and the event after it frees the pinned buffer.  Per step: one
+    # launch and one event, no second stream.
+    prepared = {}
+
+    def host_prepare(k):
+        j = k % nbuf
+        t_w = time.perf_counter()
+        if k >= nbuf:
+            copied[j].synchronize()  # the launch that copied this buffer's last contents
+        t_h = time.perf_counter()
+        cx = np.empty(B, np.int32)
+        maxc = alloc.decode_step_prepare(seqs, max_blocks, host_sl, host_tb, cx,
+                                         order_out=host_ord if use_order else None)
+        host_cx[:] = cx
+        np.copyto(h_flat[j], host_flat)
+        prepared[k] = (maxc, cx, time.perf_counter() - t_h, t_h - t_w)
+
+    def step_in_step(i):
+        host_prepare(i + 1)
+        maxc, cx = prepared.pop(i)[:2]
+        host_s.append(prepared[i + 1][2])  # this iteration's host work: the next step's
+        wait_s.append(prepared[i + 1][3])
+        ds = i % 2
+        _, d_tables, d_ctx, d_order = d_views[ds]
+        if i in ev:
+            ev[i][0].record(stream)
+        P.paged_attention_decode_step(out, q, new_k_steps[i], new_v_steps[i], k_cache, v_cache,
+                                      d_tables, d_ctx, maxc, s.scale, d_stages[1 - ds],
+                                      h_stage[(i + 1) % nbuf], args.partition, workspace,
+                                      seq_order=d_order if use_order else None)
+        if i in ev:
+            ev[i][1].record(stream)
+        copied[(i + 1) % nbuf].record(stream)
+        ctx_hist.append(cx)
+
+    if in_step:  # step 0's tables: one upload before the first launch
+        host_prepare(0)
+        P.upload_pinned(d_stages[0], h_stage[0], stream=stream)
+        copied[0].record(stream)
+        step = step_in_step
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -740,14 +794,20 @@ def main() -> int:
         "config": {
             "workload": s.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": bs, "mean_context": round(tok_t / K / B, 1),
-            "max_context": max_ctx_final, "new_tokens_per_step": B * step_tok,
+            "max_context": int(wl.ctx.max()) + (total_steps - 1) * step_tok,
+            "new_tokens_per_step": B * step_tok,
             "partition_size": part_used, "kv_bytes_per_step": int(kv_t // K),
             "decode_path": args.path, "launch_order": args.order, "chunk_tokens": chunk,
             "shared_prefix_decode": shared,
+            "upload": ("within the previous step's decode launch" if in_step else
+                       "own launch on the compute stream" if args.serial_upload else
+                       "own launch on a side stream"),
             "shared_prefix_tokens": s.shared_prefix_tokens, "num_sharers": s.num_sharers,
         },
         "roofline": {
-            "kernel": ("paged_attention_decode" + ("_write (cache write fused)" if fused_write else "")
+            "kernel": ("paged_attention_decode" + ("_step (cache write and next upload fused)" if in_step
+                                                   else "_write (cache write fused)" if fused_write
+                                                   else "")
                        + (" (single pass)" if part_used == 0 else
                           " (shared prefix once per tile of members, partition kernel + "
                           "log-sum-exp merge)" if shared else

@@ -315,6 +315,40 @@ pkv_status pkv_paged_attention_decode_write(void* out, const void* q,
                                             size_t workspace_bytes, pkv_dtype dtype,
                                             void* stream);
 
+/* The decode step's device work in one launch, for a serving loop that
+ * prepares each step's index arrays one step ahead: pkv_paged_attention_
+ * decode_write, and in the same launch a copy of next_bytes from next_src_host
+ * (pinned host memory mapped into the device's address space, e.g. a torch
+ * tensor from pin_memory()) to next_dst (device): the next step's block
+ * tables, lengths, launch order and slots.  The copy runs on the workgroups
+ * of one extra grid row, dispatched first; so the next step needs no upload
+ * launch of its own and no event between the two streams ("vLLM in
+ * Production …", section "Continuous Batching Keeps the GPU Full": the
+ * batch is re-formed at every step).  next_dst must not overlap anything
+ * this call reads or writes (the current step's arrays sit in another
+ * buffer); the caller must not change next_src_host until the call has
+ * completed.  next_bytes = 0: exactly pkv_paged_attention_decode_write.
+ * next_bytes and both addresses must be multiples of 16, the batch 1 ..
+ * 65534 sequences; PKV_ERR_INVALID_ARG (nothing launched) otherwise or if
+ * the source is not pinned, mapped host memory.  Other arguments and
+ * errors as pkv_paged_attention_decode_write. */
+pkv_status pkv_paged_attention_decode_step(void* out, const void* q,
+                                           const void* new_key, const void* new_value,
+                                           int64_t key_seq_stride, int64_t value_seq_stride,
+                                           void* k_cache, void* v_cache,
+                                           const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens,
+                                           const int32_t* seq_order,
+                                           int32_t max_context_len, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, float scale,
+                                           int32_t partition_size, void* workspace,
+                                           size_t workspace_bytes, void* next_dst,
+                                           const void* next_src_host, size_t next_bytes,
+                                           pkv_dtype dtype, void* stream);
+
 /* ------------------------------------------------------------------------
  * Chunked prefill: several new tokens per sequence attend to the paged cache
  * (long prompts are processed in pieces so that one large prefill does not

@@ -25,7 +25,7 @@ __all__ = [
     "swap_blocks", "SWAP_OUT", "SWAP_IN",
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
     "blocks_for_budget", "validate_decode_inputs", "paged_attention_decode_noalloc",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "paged_attention_decode_step",
 ]
 
 LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
@@ -67,6 +67,10 @@ EXPORTS = {
     "pkv_paged_attention_decode_write": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
                                                 _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
+    "pkv_paged_attention_decode_step": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
+                                               _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp, _sz,
+                                               _i32, _vp]),
     "pkv_longest_first_order": (_i32, [_P(_i32), _i32, _P(_i32)]),
     "pkv_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_prefill_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -391,6 +395,36 @@ def paged_attention_decode_write(out, q, new_key, new_value, k_cache, v_cache, b
         new_value.stride(0) if B else Hkv * D, k_cache.data_ptr(), v_cache.data_ptr(), idx[0],
         block_tables.shape[1], idx[1], idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N,
         float(scale), int(partition_size), ws_ptr, ws_bytes, dt, _stream_ptr(stream)), fn)
+
+
+def paged_attention_decode_step(out, q, new_key, new_value, k_cache, v_cache, block_tables,
+                                context_lens, max_context_len: int, scale: float, next_dst,
+                                next_src_pinned, partition_size: int = PARTITION_AUTO,
+                                workspace=None, stream=None, seq_order=None) -> None:
+    """``paged_attention_decode_write`` and, in the same launch, a copy of
+    the pinned host tensor ``next_src_pinned`` into the device tensor
+    ``next_dst`` (the next step's index arrays; equal byte sizes, multiples
+    of 16)."""
+    fn = "paged_attention_decode_step"
+    B, Hq = q.shape[0], q.shape[1]
+    idx = _decode_indices(block_tables, context_lens, seq_order, B, fn)
+    (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
+    qp, op = _q_out(q, out, (B, Hq, D), k_cache.dtype, fn)
+    kp = _dense_ptr(new_key, (B, Hkv, D), k_cache.dtype, "new_key", fn, rows=True)
+    vp = _dense_ptr(new_value, (B, Hkv, D), k_cache.dtype, "new_value", fn, rows=True)
+    nbytes = next_src_pinned.numel() * next_src_pinned.element_size()
+    if (next_dst.numel() * next_dst.element_size() != nbytes or not next_dst.is_cuda
+            or not next_dst.is_contiguous() or next_src_pinned.is_cuda
+            or not next_src_pinned.is_contiguous()):
+        raise ValueError(f"{fn}: next_dst must be a contiguous device tensor and "
+                         "next_src_pinned a contiguous pinned host tensor of the same byte size")
+    ws_ptr, ws_bytes = _workspace(workspace, fn)
+    _check(lib.pkv_paged_attention_decode_step(
+        op, qp, kp, vp, new_key.stride(0) if B else Hkv * D,
+        new_value.stride(0) if B else Hkv * D, k_cache.data_ptr(), v_cache.data_ptr(), idx[0],
+        block_tables.shape[1], idx[1], idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N,
+        float(scale), int(partition_size), ws_ptr, ws_bytes, next_dst.data_ptr(),
+        next_src_pinned.data_ptr(), nbytes, dt, _stream_ptr(stream)), fn)
 
 
 def upload_pinned(dst, src_pinned, stream=None) -> None:

@@ -96,9 +96,11 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+}  // namespace
+
 // Device address of pinned, mapped host memory; nullptr (and no sticky
 // runtime error left behind) if the pointer is not such memory.
-void* mapped(void* host) {
+void* mapped_host(void* host) {
   void* dev = nullptr;
   const hipError_t e = hipHostGetDevicePointer(&dev, host, 0);
   if (e != hipSuccess || !dev) {
@@ -108,7 +110,6 @@ void* mapped(void* host) {
   return dev;
 }
 
-}  // namespace
 }  // namespace pkv
 
 using pkv::fail;
@@ -211,8 +212,8 @@ extern "C" pkv_status pkv_swap_blocks(void* k_cache, void* v_cache, void* k_host
   if (!pkv::aligned16(k_cache) || !pkv::aligned16(v_cache) || !pkv::aligned16(k_host) ||
       !pkv::aligned16(v_host))
     return fail(PKV_ERR_INVALID_ARG, "swap_blocks: caches and pools must be 16-byte aligned");
-  void* kh = pkv::mapped(k_host);
-  void* vh = pkv::mapped(v_host);
+  void* kh = pkv::mapped_host(k_host);
+  void* vh = pkv::mapped_host(v_host);
   if (!kh || !vh)
     return fail(PKV_ERR_INVALID_ARG,
                 "swap_blocks: the host pools must be pinned, device-mapped host memory");
@@ -238,7 +239,7 @@ extern "C" pkv_status pkv_upload_pinned(void* dst, const void* src_host, size_t 
   if (bytes % 16 || !pkv::aligned16(dst) || !pkv::aligned16(src_host))
     return fail(PKV_ERR_INVALID_ARG,
                 "upload_pinned: size (%zu) and both addresses must be multiples of 16 bytes", bytes);
-  void* src_dev = pkv::mapped(const_cast<void*>(src_host));
+  void* src_dev = pkv::mapped_host(const_cast<void*>(src_host));
   if (!src_dev)
     return fail(PKV_ERR_INVALID_ARG,
                 "upload_pinned: source is not pinned, device-mapped host memory");

@@ -46,7 +46,34 @@ struct NewRows {
   const void* new_v;
   int64_t k_stride;  // elements between sequences' rows
   int64_t v_stride;
+  // The next step's index arrays, copied within the launch (decode step
+  // only): pf_n16 16-byte pieces from pinned host memory (device-mapped
+  // address pf_src) to pf_dst by the workgroups of the first pf_rows grid
+  // rows; the sequences' rows follow them.
+  const uint4* pf_src;
+  uint4* pf_dst;
+  int64_t pf_n16;
+  int32_t pf_rows;
 };
+
+// The next step's upload by the workgroups of the first w.pf_rows grid rows:
+// each thread issues up to four 16-byte loads over the host link before its
+// stores.
+__device__ __forceinline__ void copy_next_step(const NewRows& w) {
+  const int64_t nthreads = int64_t(gridDim.x) * gridDim.y * w.pf_rows * blockDim.x;
+  const int64_t t =
+      ((int64_t(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x +
+      threadIdx.x;
+  for (int64_t i = t; i < w.pf_n16; i += 4 * nthreads) {
+    uint4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i + k * nthreads < w.pf_n16) v[k] = w.pf_src[i + k * nthreads];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i + k * nthreads < w.pf_n16) w.pf_dst[i + k * nthreads] = v[k];
+  }
+}
 
 // Stores a lane's fragment (the counterpart of load_frag).
 template <int WORDS>
@@ -82,11 +109,17 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a, NewRow
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4;
   const int r = lane & 15;
+  if constexpr (WRITE) {
+    if (int(blockIdx.z) < w.pf_rows) {  // the next step's upload
+      copy_next_step(w);
+      return;
+    }
+  }
   const int part = blockIdx.x;
   const int kvh0 = blockIdx.y * HG;     // first kv head of the workgroup
   const int kvh = kvh0 + wave % HG;     // this wave's kv head
   const int stream = wave / HG;         // this wave's chunk stream
-  const int b = seq_of(a, blockIdx.z);
+  const int b = seq_of(a, int(blockIdx.z) - (WRITE ? w.pf_rows : 0));
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
 
@@ -416,6 +449,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
+  if constexpr (WRITE) {
+    if (int(blockIdx.z) < w.pf_rows) {  // the next step's upload
+      copy_next_step(w);
+      return;
+    }
+  }
 
   // Shared-prefix rows: a tile of 16 / G members sharing the prefix; its
   // operand columns are (member, query head) pairs, and it computes the
@@ -443,7 +482,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
     return (unsigned)s < (unsigned)a.num_seqs ? s : 0;
   };
   const int part = group ? 0 : int(blockIdx.x);
-  const int b = group ? member_seq(tile * mpg) : seq_of(a, int(blockIdx.z) - a.seq_z0);
+  const int b = group ? member_seq(tile * mpg)
+                      : seq_of(a, int(blockIdx.z) - a.seq_z0 - (WRITE ? w.pf_rows : 0));
 
   // The 16 operand columns are the G query heads of this kv head (padded
   // with zero columns); the query sees the sequence's whole context.
@@ -811,13 +851,13 @@ hipError_t launch_valu(const AttnArgs& a, const NewRows& w, int num_seqs, hipStr
                        int grid_parts) {
   if constexpr (sizeof(T) == 2 && G <= 2) {
     if (a.num_kv_heads % 4 == 0) {  // wide_layout() decides the same
-      const dim3 grid = work_grid(grid_parts, a.num_kv_heads / kValuHG, num_seqs);
+      const dim3 grid = work_grid(grid_parts, a.num_kv_heads / kValuHG, num_seqs + w.pf_rows);
       hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kValuNW, kValuHG, WRITE>), grid,
                          dim3(kValuNW * 64), 0, st, a, w);
       return hipGetLastError();
     }
   }
-  const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
+  const dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs + w.pf_rows);
   hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, kNW, 1, WRITE>), grid, dim3(kNW * 64), 0, st,
                      a, w);
   return hipGetLastError();
@@ -836,11 +876,11 @@ template <bool WRITE, int D, int BS>
 hipError_t launch_mfma(const AttnArgs& a, const NewRows& w, int num_seqs, hipStream_t st,
                        int grid_parts) {
   if (kMfmaHG > 1 && a.num_kv_heads % kMfmaHG == 0) {
-    const dim3 grid = work_grid(grid_parts, a.num_kv_heads / kMfmaHG, num_seqs);
+    const dim3 grid = work_grid(grid_parts, a.num_kv_heads / kMfmaHG, num_seqs + w.pf_rows);
     hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kMfmaNW, kMfmaHG, WRITE>), grid,
                        dim3(kMfmaNW * 64), 0, st, a, w);
   } else {
-    dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs);
+    dim3 grid = work_grid(grid_parts, a.num_kv_heads, num_seqs + w.pf_rows);
     AttnArgs ag = a;
     if (!WRITE && a.members != nullptr && a.num_members > 0) {
       // shared-prefix tiles: grid.x * num_kv_heads workgroups per row, in
@@ -1174,6 +1214,62 @@ extern "C" pkv_status pkv_paged_attention_decode_shared_prefix(
                      num_members);
 }
 
+namespace {
+
+// The decode step with its cache write, and optionally the next step's
+// upload, in one launch: the checks of both entry points.
+pkv_status decode_write_call(const char* fn, void* out, const void* q, const void* new_key,
+                             const void* new_value, int64_t key_seq_stride,
+                             int64_t value_seq_stride, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* seq_order,
+                             int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, float scale, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* next_dst,
+                             const void* next_src_host, size_t next_bytes, pkv_dtype dtype,
+                             void* stream) {
+  const int64_t esize = dtype == PKV_F32 ? 4 : 2;
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if (num_seqs > 0 && (!new_key || !new_value))
+    return fail(PKV_ERR_INVALID_ARG, "%s: NULL new key/value", fn);
+  if (key_seq_stride < row || value_seq_stride < row || (key_seq_stride * esize) % 16 ||
+      (value_seq_stride * esize) % 16 || (reinterpret_cast<uintptr_t>(new_key) & 15u) ||
+      (reinterpret_cast<uintptr_t>(new_value) & 15u) ||
+      (reinterpret_cast<uintptr_t>(k_cache) & 15u) || (reinterpret_cast<uintptr_t>(v_cache) & 15u))
+    return fail(PKV_ERR_INVALID_ARG,
+                "%s: sequence strides (%lld, %lld) must be >= %lld "
+                "elements and multiples of 16 bytes, pointers 16-byte aligned", fn,
+                (long long)key_seq_stride, (long long)value_seq_stride, (long long)row);
+  pkv::NewRows w{new_key, new_value, key_seq_stride, value_seq_stride, nullptr, nullptr, 0, 0};
+  if (next_bytes > 0) {
+    if (!next_dst || !next_src_host || next_bytes % 16 ||
+        (reinterpret_cast<uintptr_t>(next_dst) & 15u) ||
+        (reinterpret_cast<uintptr_t>(next_src_host) & 15u))
+      return fail(PKV_ERR_INVALID_ARG,
+                  "%s: the next step's upload needs non-NULL 16-byte aligned buffers and a "
+                  "multiple of 16 bytes (%zu)", fn, next_bytes);
+    void* src_dev = pkv::mapped_host(const_cast<void*>(next_src_host));
+    if (!src_dev)
+      return fail(PKV_ERR_INVALID_ARG, "%s: next_src_host is not pinned, device-mapped host memory",
+                  fn);
+    w.pf_src = static_cast<const uint4*>(src_dev);
+    w.pf_dst = static_cast<uint4*>(next_dst);
+    w.pf_n16 = int64_t(next_bytes / 16);
+    w.pf_rows = 1;
+    if (num_seqs == 0 || num_seqs > 65534)
+      return fail(PKV_ERR_INVALID_ARG,
+                  "%s: the next step's upload needs 1 .. 65534 sequences (its grid row comes "
+                  "first), got %d", fn, num_seqs);
+  }
+  return decode_call(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, seq_order, max_context_len, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                     workspace, workspace_bytes, dtype, stream, &w);
+}
+
+}  // namespace
+
 extern "C" pkv_status pkv_paged_attention_decode_write(
     void* out, const void* q, const void* new_key, const void* new_value,
     int64_t key_seq_stride, int64_t value_seq_stride, void* k_cache, void* v_cache,
@@ -1182,23 +1278,28 @@ extern "C" pkv_status pkv_paged_attention_decode_write(
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
     void* stream) {
-  const int64_t esize = dtype == PKV_F32 ? 4 : 2;
-  const int64_t row = int64_t(num_kv_heads) * head_dim;
-  if (num_seqs > 0 && (!new_key || !new_value))
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode_write: NULL new key/value");
-  if (key_seq_stride < row || value_seq_stride < row || (key_seq_stride * esize) % 16 ||
-      (value_seq_stride * esize) % 16 || (reinterpret_cast<uintptr_t>(new_key) & 15u) ||
-      (reinterpret_cast<uintptr_t>(new_value) & 15u) ||
-      (reinterpret_cast<uintptr_t>(k_cache) & 15u) || (reinterpret_cast<uintptr_t>(v_cache) & 15u))
-    return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode_write: sequence strides (%lld, %lld) must be >= %lld "
-                "elements and multiples of 16 bytes, pointers 16-byte aligned",
-                (long long)key_seq_stride, (long long)value_seq_stride, (long long)row);
-  const pkv::NewRows w{new_key, new_value, key_seq_stride, value_seq_stride};
-  return decode_call("paged_attention_decode_write", out, q, k_cache, v_cache, block_tables,
-                     max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
-                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
-                     partition_size, workspace, workspace_bytes, dtype, stream, &w);
+  return decode_write_call("paged_attention_decode_write", out, q, new_key, new_value,
+                           key_seq_stride, value_seq_stride, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
+                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                           partition_size, workspace, workspace_bytes, nullptr, nullptr, 0, dtype,
+                           stream);
+}
+
+extern "C" pkv_status pkv_paged_attention_decode_step(
+    void* out, const void* q, const void* new_key, const void* new_value,
+    int64_t key_seq_stride, int64_t value_seq_stride, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* next_dst,
+    const void* next_src_host, size_t next_bytes, pkv_dtype dtype, void* stream) {
+  return decode_write_call("paged_attention_decode_step", out, q, new_key, new_value,
+                           key_seq_stride, value_seq_stride, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
+                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                           partition_size, workspace, workspace_bytes, next_dst, next_src_host,
+                           next_bytes, dtype, stream);
 }
 
 // ---------------------------------------------------------------------------

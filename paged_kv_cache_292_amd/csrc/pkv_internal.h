@@ -15,4 +15,8 @@ pkv_status fail(pkv_status st, const char* fmt, ...)
 // Returns PKV_OK (the last error message is kept).
 pkv_status ok();
 
+// Device address of pinned host memory mapped into the device's address
+// space (hipHostMalloc, torch's pin_memory()), nullptr for other memory.
+void* mapped_host(void* host);
+
 }  // namespace pkv

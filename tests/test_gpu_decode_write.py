@@ -141,3 +141,67 @@ def test_fused_write_zero_context_and_launch_order(decode_path):
     assert np.array_equal(_bits(kd), _bits(ko)) and np.array_equal(_bits(vd), _bits(vo))
     assert (OA.widen(got, s.dtype)[2] == 0).all()
     assert_close(OA.widen(got, s.dtype), ref, s.dtype, "fused, zero context, ordered")
+
+
+def _run_step(s, wl, tables, ctx, kc, vc, part, nbytes, seed, order=None):
+    """pkv_paged_attention_decode_step with a seeded pinned source of nbytes."""
+    kd, vd = to_dev(kc, s.dtype), to_dev(vc, s.dtype)
+    q = to_dev(wl.q, s.dtype)
+    nk, nv = to_dev(wl.new_k, s.dtype), to_dev(wl.new_v, s.dtype)
+    out = torch.empty_like(q)
+    mx = int(ctx.max())
+    wsb = P.decode_workspace_bytes(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                   s.block_size, mx, part, P.F32 if s.dtype == "f32" else P.BF16)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    src_np = np.random.default_rng(seed).integers(0, 256, nbytes, dtype=np.uint8)
+    src = torch.from_numpy(src_np).pin_memory()
+    dst = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    td, cd = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+    so = torch.from_numpy(order).cuda() if order is not None else None
+    P.paged_attention_decode_step(out, q, nk, nv, kd, vd, td, cd, mx, s.scale, dst, src, part, ws,
+                                  seq_order=so)
+    torch.cuda.synchronize()
+    return (from_dev(out, s.dtype), from_dev(kd, s.dtype), from_dev(vd, s.dtype),
+            dst.cpu().numpy(), src_np)
+
+
+@pytest.mark.parametrize("name", ["llama13b", "gqa_prefix", "long_splitk", "f32_g2_d128"])
+@pytest.mark.parametrize("part", [0, P.PARTITION_AUTO])
+def test_decode_step_uploads_the_next_arrays_in_the_same_launch(name, part, decode_path):
+    """The decode step with the next step's upload: output and caches
+    bit-identical to the fused-write call (the same kernels and work), the
+    uploaded bytes exact, for uploads larger than one grid row's threads."""
+    s = CASES[name]
+    wl, slots, tables, ctx, kc, vc = _setup(s)
+    ko, vo = OC.reshape_and_cache(wl.new_k, wl.new_v, kc, vc, slots)
+    ref = OA.paged_decode(wl.q, ko, vo, tables, ctx, s.scale, s.dtype)
+    order = P.longest_first_order(ctx)
+    paths = [P.PATH_AUTO] if s.dtype == "f32" else [P.PATH_VALU, P.PATH_MFMA]
+    for path in paths:
+        decode_path(path)
+        for nbytes in (16, 16 * 40963):  # one piece; more than four per thread of the row
+            log(f"decode step {name} partition={part} path={path} upload={nbytes} B")
+            got, kd, vd, dst, src = _run_step(s, wl, tables, ctx, kc, vc, part, nbytes,
+                                              seed=nbytes, order=order)
+            assert np.array_equal(dst, src), "the next step's arrays"
+            assert np.array_equal(_bits(kd), _bits(ko)) and np.array_equal(_bits(vd), _bits(vo))
+            fused, _, _ = _run(s, wl, tables, ctx, kc, vc, part, True, order=order)
+            assert np.array_equal(_bits(got), _bits(fused)), "decode step vs fused write"
+            assert_close(OA.widen(got, s.dtype), ref, s.dtype, f"step {name} p{part} path{path}")
+
+
+def test_decode_step_refuses_pageable_memory_before_launch():
+    s = CASES["llama13b"]
+    wl, slots, tables, ctx, kc, vc = _setup(s)
+    kd, vd = to_dev(kc, s.dtype), to_dev(vc, s.dtype)
+    q = to_dev(wl.q, s.dtype)
+    out = torch.full_like(q, 5.0)
+    dst = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(P.PkvError, match="INVALID_ARG"):
+        P.paged_attention_decode_step(out, q, to_dev(wl.new_k, s.dtype), to_dev(wl.new_v, s.dtype),
+                                      kd, vd, torch.from_numpy(tables).cuda(),
+                                      torch.from_numpy(ctx).cuda(), int(ctx.max()), s.scale, dst,
+                                      torch.zeros(64, dtype=torch.uint8), 0)
+    torch.cuda.synchronize()
+    assert (out.float() == 5.0).all()
+    assert np.array_equal(from_dev(kd, s.dtype), kc)

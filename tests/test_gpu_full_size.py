@@ -5,7 +5,8 @@ Each test sets up the first timed step of ``bench.py --shape i`` the way the
 benchmark does: the pool sized with the benchmark's growth room, tables
 padded to the width of the last step, the longest-first launch order from
 the allocator, automatic partitioning, and for the LLaMA-13B batch the
-decode call that also writes the step's new tokens.  The product allocator's
+decode step that also writes the step's new tokens and uploads the next
+step's arrays.  The product allocator's
 slots, tables, lengths and order must equal the oracle allocator's (and a
 stable longest-first sort) bit for bit; then every (sequence, query head)
 row of every launch is compared with the fp64 oracle
@@ -61,9 +62,12 @@ def bench_first_step(idx: int) -> BenchStep:
     """Step 0 of ``bench.py --shape idx`` on both allocators."""
     s = W.shape(idx)
     step_tok = s.chunk if s.chunk else (1 if s.new_tokens else 0)
-    wl = W.make_workload(s, extra_tokens=BENCH_STEPS * step_tok)
+    # a decode step with new tokens prepares one step ahead (its launch
+    # uploads the next step's arrays): growth room for one step more
+    ahead = 1 if s.new_tokens and not s.chunk else 0
+    wl = W.make_workload(s, extra_tokens=(BENCH_STEPS + ahead) * step_tok)
     B, bs = s.num_seqs, s.block_size
-    final_ctx = wl.ctx + (BENCH_STEPS - 1) * step_tok
+    final_ctx = wl.ctx + (BENCH_STEPS - 1 + ahead) * step_tok
     max_blocks = int(((final_ctx + bs - 1) // bs).max())
     o = OAL.BlockAllocator(wl.num_blocks, bs, wl.free_order)
     o.replay(wl.ops)
@@ -166,24 +170,55 @@ def test_full_tiny_and_llama7b(idx):
     assert_close(_decode(st, d, P.PARTITION_AUTO), ref, st.s.dtype, f"{st.s.name} full, AUTO")
 
 
-def test_full_llama13b_fused_write():
-    """The benchmark's gate call: cache write and decode in one launch, all
-    128 sequences, longest-first order, automatic partitioning.  Caches
-    bit-exact against the oracle's cache write, every row within tolerance."""
+def _next_step_arrays(st):
+    """The second step's slots, tables, lengths and longest-first order as
+    the benchmark stages them (one byte buffer), from the oracle allocator
+    replayed to the end of the first step."""
+    s = st.s
+    B, bs = s.num_seqs, s.block_size
+    o = OAL.BlockAllocator(st.wl.num_blocks, bs, st.wl.free_order)
+    o.replay(st.wl.ops)
+    for b in range(B):
+        o.append(b, 1)
+    slots = np.array([o.append(b, 1)[0] for b in range(B)], dtype=np.int64)
+    tables, ctx = o.build_block_tables(list(range(B)), st.tables.shape[1], pad=-1)
+    parts = [slots.view(np.uint8), tables.view(np.uint8).ravel(), ctx.view(np.uint8),
+             _longest_first(ctx).view(np.uint8)]
+    buf = np.concatenate(parts)
+    return np.concatenate([buf, np.zeros((-len(buf)) % 16, np.uint8)])
+
+
+def test_full_llama13b_decode_step():
+    """The benchmark's gate call: cache write, decode and the next step's
+    upload in one launch, all 128 sequences, longest-first order, automatic
+    partitioning.  Caches bit-exact against the oracle's cache write, the
+    uploaded arrays bit-exact, every row within tolerance; the same through
+    the fused write alone."""
     st = bench_first_step(2)
     s = st.s
-    log(f"full size {s.name}: fused write + decode, B={s.num_seqs}")
+    log(f"full size {s.name}: decode step (write + decode + next upload), B={s.num_seqs}")
     ref = _oracle(st)
+    nxt = _next_step_arrays(st)
+    src = torch.from_numpy(nxt).pin_memory()
+    dst = torch.zeros(len(nxt), dtype=torch.uint8, device="cuda")
     d = Dev(st, write=False)
     out = torch.empty_like(d.q)
-    P.paged_attention_decode_write(out, d.q, d.new_k, d.new_v, d.k, d.v, d.tables, d.ctx,
-                                   d.max_ctx, s.scale, P.PARTITION_AUTO,
-                                   d.workspace(s, P.PARTITION_AUTO), seq_order=d.order)
+    P.paged_attention_decode_step(out, d.q, d.new_k, d.new_v, d.k, d.v, d.tables, d.ctx,
+                                  d.max_ctx, s.scale, dst, src, P.PARTITION_AUTO,
+                                  d.workspace(s, P.PARTITION_AUTO), seq_order=d.order)
     torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), nxt), "the next step's arrays"
     assert np.array_equal(_bits(from_dev(d.k, s.dtype)), _bits(st.k_after)), "K cache after write"
     assert np.array_equal(_bits(from_dev(d.v, s.dtype)), _bits(st.v_after)), "V cache after write"
-    assert_close(OA.widen(from_dev(out, s.dtype), s.dtype), ref, s.dtype,
-                 f"{s.name} full, fused write, AUTO")
+    step_out = OA.widen(from_dev(out, s.dtype), s.dtype)
+    assert_close(step_out, ref, s.dtype, f"{s.name} full, decode step, AUTO")
+    d1 = Dev(st, write=False)
+    out1 = torch.empty_like(d1.q)
+    P.paged_attention_decode_write(out1, d1.q, d1.new_k, d1.new_v, d1.k, d1.v, d1.tables, d1.ctx,
+                                   d1.max_ctx, s.scale, P.PARTITION_AUTO,
+                                   d1.workspace(s, P.PARTITION_AUTO), seq_order=d1.order)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(OA.widen(from_dev(out1, s.dtype), s.dtype), step_out)
     # the separate write then decode (bench.py --separate-write), and single pass
     d2 = Dev(st, write=True)
     assert_close(_decode(st, d2, P.PARTITION_AUTO), ref, s.dtype, f"{s.name} full, separate write")
