@@ -51,9 +51,10 @@ def _args():
                     help="upload each step's tables on the compute stream instead of a side "
                          "stream overlapped with the previous step's attention")
     ap.add_argument("--upload-kernel", action="store_true",
-                    help="decode steps with new tokens: upload each step's tables with their own "
-                         "upload launch (side stream, or --serial-upload) instead of within the "
-                         "previous step's decode launch (paged_attention_decode_step)")
+                    help="decode steps (not the shared-prefix call): upload each step's tables "
+                         "with their own upload launch (side stream, or --serial-upload) instead "
+                         "of within the previous step's decode launch "
+                         "(paged_attention_decode_step)")
     ap.add_argument("--staging-depth", type=int, default=8,
                     help="pinned staging buffers in flight (steps the host may run ahead)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
@@ -495,10 +496,12 @@ def main() -> int:
     chunk = s.chunk  # > 0: a chunked-prefill step of this many tokens per sequence
     step_tok = chunk if chunk else step_new  # tokens each sequence gains per step
     # decode steps with new tokens write them inside the decode launch, and
-    # (unless --upload-kernel) that launch also uploads the next step's
-    # tables, which the host prepares one step ahead
+    # (unless --upload-kernel) every decode launch but the shared-prefix one
+    # also uploads the next step's tables, which the host prepares one step
+    # ahead
     fused_write = bool(step_new) and not s.chunk and not args.separate_write
-    in_step = fused_write and not args.upload_kernel and not args.serial_upload
+    in_step = ((fused_write or not (step_new or s.chunk or args.shared_prefix))
+               and not args.upload_kernel and not args.serial_upload)
     # growth room: in_step prepares one step more than it decodes
     wl = W.make_workload(s, extra_tokens=(total_steps + int(in_step)) * step_tok)
     B, Hq, Hkv, D, bs = s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size
@@ -709,8 +712,14 @@ def main() -> int:
             copied[j].synchronize()  # the launch that copied this buffer's last contents
         t_h = time.perf_counter()
         cx = np.empty(B, np.int32)
-        maxc = alloc.decode_step_prepare(seqs, max_blocks, host_sl, host_tb, cx,
-                                         order_out=host_ord if use_order else None)
+        if step_new:
+            maxc = alloc.decode_step_prepare(seqs, max_blocks, host_sl, host_tb, cx,
+                                             order_out=host_ord if use_order else None)
+        else:
+            alloc.build_block_tables(seqs, max_blocks, pad=-1, tables_out=host_tb, ctx_out=cx)
+            maxc = int(cx.max())
+            if use_order:
+                host_ord[:] = P.longest_first_order(cx)
         host_cx[:] = cx
         np.copyto(h_flat[j], host_flat)
         prepared[k] = (maxc, cx, time.perf_counter() - t_h, t_h - t_w)
@@ -724,7 +733,8 @@ def main() -> int:
         _, d_tables, d_ctx, d_order = d_views[ds]
         if i in ev:
             ev[i][0].record(stream)
-        P.paged_attention_decode_step(out, q, new_k_steps[i], new_v_steps[i], k_cache, v_cache,
+        nk, nv = (new_k_steps[i], new_v_steps[i]) if step_new else (None, None)
+        P.paged_attention_decode_step(out, q, nk, nv, k_cache, v_cache,
                                       d_tables, d_ctx, maxc, s.scale, d_stages[1 - ds],
                                       h_stage[(i + 1) % nbuf], args.partition, workspace,
                                       seq_order=d_order if use_order else None)
@@ -805,9 +815,10 @@ def main() -> int:
             "shared_prefix_tokens": s.shared_prefix_tokens, "num_sharers": s.num_sharers,
         },
         "roofline": {
-            "kernel": ("paged_attention_decode" + ("_step (cache write and next upload fused)" if in_step
-                                                   else "_write (cache write fused)" if fused_write
-                                                   else "")
+            "kernel": ("paged_attention_decode"
+                       + ("_step (cache write and next upload fused)" if in_step and fused_write
+                          else "_step (next upload fused)" if in_step
+                          else "_write (cache write fused)" if fused_write else "")
                        + (" (single pass)" if part_used == 0 else
                           " (shared prefix once per tile of members, partition kernel + "
                           "log-sum-exp merge)" if shared else

@@ -328,6 +328,10 @@ pkv_status pkv_paged_attention_decode_write(void* out, const void* q,
  * this call reads or writes (the current step's arrays sit in another
  * buffer); the caller must not change next_src_host until the call has
  * completed.  next_bytes = 0: exactly pkv_paged_attention_decode_write.
+ * new_key and new_value both NULL: a step without new tokens (strides
+ * ignored, nothing written into the caches): the attention of
+ * pkv_paged_attention_decode plus the upload; only one of them NULL is
+ * PKV_ERR_INVALID_ARG.
  * next_bytes and both addresses must be multiples of 16, the batch 1 ..
  * 65534 sequences; PKV_ERR_INVALID_ARG (nothing launched) otherwise or if
  * the source is not pinned, mapped host memory.  Other arguments and

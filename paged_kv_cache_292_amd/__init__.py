@@ -404,14 +404,23 @@ def paged_attention_decode_step(out, q, new_key, new_value, k_cache, v_cache, bl
     """``paged_attention_decode_write`` and, in the same launch, a copy of
     the pinned host tensor ``next_src_pinned`` into the device tensor
     ``next_dst`` (the next step's index arrays; equal byte sizes, multiples
-    of 16)."""
+    of 16).  ``new_key`` and ``new_value`` both None: a step without new
+    tokens (``paged_attention_decode`` plus the upload)."""
     fn = "paged_attention_decode_step"
     B, Hq = q.shape[0], q.shape[1]
     idx = _decode_indices(block_tables, context_lens, seq_order, B, fn)
     (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
     qp, op = _q_out(q, out, (B, Hq, D), k_cache.dtype, fn)
-    kp = _dense_ptr(new_key, (B, Hkv, D), k_cache.dtype, "new_key", fn, rows=True)
-    vp = _dense_ptr(new_value, (B, Hkv, D), k_cache.dtype, "new_value", fn, rows=True)
+    if new_key is None and new_value is None:
+        kp = vp = None
+        ks = vs = 0
+    else:
+        if new_key is None or new_value is None:
+            raise ValueError(f"{fn}: new_key and new_value are both tensors or both None")
+        kp = _dense_ptr(new_key, (B, Hkv, D), k_cache.dtype, "new_key", fn, rows=True)
+        vp = _dense_ptr(new_value, (B, Hkv, D), k_cache.dtype, "new_value", fn, rows=True)
+        ks = new_key.stride(0) if B else Hkv * D
+        vs = new_value.stride(0) if B else Hkv * D
     nbytes = next_src_pinned.numel() * next_src_pinned.element_size()
     if (next_dst.numel() * next_dst.element_size() != nbytes or not next_dst.is_cuda
             or not next_dst.is_contiguous() or next_src_pinned.is_cuda
@@ -420,8 +429,7 @@ def paged_attention_decode_step(out, q, new_key, new_value, k_cache, v_cache, bl
                          "next_src_pinned a contiguous pinned host tensor of the same byte size")
     ws_ptr, ws_bytes = _workspace(workspace, fn)
     _check(lib.pkv_paged_attention_decode_step(
-        op, qp, kp, vp, new_key.stride(0) if B else Hkv * D,
-        new_value.stride(0) if B else Hkv * D, k_cache.data_ptr(), v_cache.data_ptr(), idx[0],
+        op, qp, kp, vp, ks, vs, k_cache.data_ptr(), v_cache.data_ptr(), idx[0],
         block_tables.shape[1], idx[1], idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N,
         float(scale), int(partition_size), ws_ptr, ws_bytes, next_dst.data_ptr(),
         next_src_pinned.data_ptr(), nbytes, dt, _stream_ptr(stream)), fn)

@@ -109,17 +109,15 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(AttnArgs a, NewRow
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4;
   const int r = lane & 15;
-  if constexpr (WRITE) {
-    if (int(blockIdx.z) < w.pf_rows) {  // the next step's upload
-      copy_next_step(w);
-      return;
-    }
+  if (int(blockIdx.z) < w.pf_rows) {  // the next step's upload
+    copy_next_step(w);
+    return;
   }
   const int part = blockIdx.x;
   const int kvh0 = blockIdx.y * HG;     // first kv head of the workgroup
   const int kvh = kvh0 + wave % HG;     // this wave's kv head
   const int stream = wave / HG;         // this wave's chunk stream
-  const int b = seq_of(a, int(blockIdx.z) - (WRITE ? w.pf_rows : 0));
+  const int b = seq_of(a, int(blockIdx.z) - w.pf_rows);
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
 
@@ -449,11 +447,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
-  if constexpr (WRITE) {
-    if (int(blockIdx.z) < w.pf_rows) {  // the next step's upload
-      copy_next_step(w);
-      return;
-    }
+  if (int(blockIdx.z) < w.pf_rows) {  // the next step's upload (never with shared-prefix rows)
+    copy_next_step(w);
+    return;
   }
 
   // Shared-prefix rows: a tile of 16 / G members sharing the prefix; its
@@ -483,7 +479,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   };
   const int part = group ? 0 : int(blockIdx.x);
   const int b = group ? member_seq(tile * mpg)
-                      : seq_of(a, int(blockIdx.z) - a.seq_z0 - (WRITE ? w.pf_rows : 0));
+                      : seq_of(a, int(blockIdx.z) - a.seq_z0 - w.pf_rows);
 
   // The 16 operand columns are the G query heads of this kv head (padded
   // with zero columns); the query sees the sequence's whole context.
@@ -1037,7 +1033,7 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
                        int32_t partition_size, void* workspace, size_t workspace_bytes,
                        pkv_dtype dtype, void* stream, const pkv::NewRows* w,
                        const int32_t* members = nullptr, const int32_t* member_flag = nullptr,
-                       int32_t num_members = 0) {
+                       int32_t num_members = 0, const pkv::NewRows* upload_only = nullptr) {
   if (dtype != PKV_F32 && dtype != PKV_BF16)
     return fail(PKV_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dtype));
   if (num_seqs < 0 || num_seqs > 65535)
@@ -1146,8 +1142,8 @@ pkv_status decode_call(const char* fn, void* out, const void* q, const void* k_c
   const bool f32 = dtype == PKV_F32;
   hipError_t e =
       w ? pkv::dispatch_all<true>(a, *w, f32, head_dim, block_size, G, num_seqs, st, grid_parts)
-        : pkv::dispatch_all<false>(a, pkv::NewRows{}, f32, head_dim, block_size, G, num_seqs, st,
-                                   grid_parts);
+        : pkv::dispatch_all<false>(a, upload_only ? *upload_only : pkv::NewRows{}, f32, head_dim,
+                                   block_size, G, num_seqs, st, grid_parts);
   if (e == hipSuccess && partition > 0) {
     if (head_dim == 64)
       e = f32 ? pkv::launch_reduce<float, 64>(a, num_seqs, st)
@@ -1217,8 +1213,10 @@ extern "C" pkv_status pkv_paged_attention_decode_shared_prefix(
 namespace {
 
 // The decode step with its cache write, and optionally the next step's
-// upload, in one launch: the checks of both entry points.
-pkv_status decode_write_call(const char* fn, void* out, const void* q, const void* new_key,
+// upload, in one launch: the checks of both entry points.  rows_optional:
+// new_key and new_value both NULL mean a step without new tokens (no cache
+// write, the attention of pkv_paged_attention_decode).
+pkv_status decode_write_call(const char* fn, bool rows_optional, void* out, const void* q, const void* new_key,
                              const void* new_value, int64_t key_seq_stride,
                              int64_t value_seq_stride, void* k_cache, void* v_cache,
                              const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -1231,12 +1229,13 @@ pkv_status decode_write_call(const char* fn, void* out, const void* q, const voi
                              void* stream) {
   const int64_t esize = dtype == PKV_F32 ? 4 : 2;
   const int64_t row = int64_t(num_kv_heads) * head_dim;
-  if (num_seqs > 0 && (!new_key || !new_value))
+  const bool write = !rows_optional || new_key || new_value;
+  if (num_seqs > 0 && write && (!new_key || !new_value))
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL new key/value", fn);
-  if (key_seq_stride < row || value_seq_stride < row || (key_seq_stride * esize) % 16 ||
+  if (write && (key_seq_stride < row || value_seq_stride < row || (key_seq_stride * esize) % 16 ||
       (value_seq_stride * esize) % 16 || (reinterpret_cast<uintptr_t>(new_key) & 15u) ||
       (reinterpret_cast<uintptr_t>(new_value) & 15u) ||
-      (reinterpret_cast<uintptr_t>(k_cache) & 15u) || (reinterpret_cast<uintptr_t>(v_cache) & 15u))
+      (reinterpret_cast<uintptr_t>(k_cache) & 15u) || (reinterpret_cast<uintptr_t>(v_cache) & 15u)))
     return fail(PKV_ERR_INVALID_ARG,
                 "%s: sequence strides (%lld, %lld) must be >= %lld "
                 "elements and multiples of 16 bytes, pointers 16-byte aligned", fn,
@@ -1265,7 +1264,8 @@ pkv_status decode_write_call(const char* fn, void* out, const void* q, const voi
   return decode_call(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, seq_order, max_context_len, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
-                     workspace, workspace_bytes, dtype, stream, &w);
+                     workspace, workspace_bytes, dtype, stream, write ? &w : nullptr, nullptr,
+                     nullptr, 0, write ? nullptr : &w);
 }
 
 }  // namespace
@@ -1278,7 +1278,7 @@ extern "C" pkv_status pkv_paged_attention_decode_write(
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
     void* stream) {
-  return decode_write_call("paged_attention_decode_write", out, q, new_key, new_value,
+  return decode_write_call("paged_attention_decode_write", false, out, q, new_key, new_value,
                            key_seq_stride, value_seq_stride, k_cache, v_cache, block_tables,
                            max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
                            num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
@@ -1294,7 +1294,7 @@ extern "C" pkv_status pkv_paged_attention_decode_step(
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     int32_t partition_size, void* workspace, size_t workspace_bytes, void* next_dst,
     const void* next_src_host, size_t next_bytes, pkv_dtype dtype, void* stream) {
-  return decode_write_call("paged_attention_decode_step", out, q, new_key, new_value,
+  return decode_write_call("paged_attention_decode_step", true, out, q, new_key, new_value,
                            key_seq_stride, value_seq_stride, k_cache, v_cache, block_tables,
                            max_blocks_per_seq, context_lens, seq_order, max_context_len, num_seqs,
                            num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,

@@ -403,6 +403,30 @@ def test_decode_write_rejects_bad_arguments_before_launch(kw, code):
     assert P.lib.pkv_last_error().decode()
 
 
+def _decode_step(nk, nv, **kw):
+    a = dict(out=0x100000, q=0x200000, ks=512, vs=512)
+    a.update(kw)
+    return P.lib.pkv_paged_attention_decode_step(
+        a["out"], a["q"], nk, nv, a["ks"], a["vs"], 0x500000, 0x600000, 0x700000, 4, 0x800000,
+        None, 64, 2, 4, 4, 128, 16, 8, 0.1, 0, 0, 0, None, None, 0, P.BF16, None)
+
+
+def test_decode_step_without_new_rows_skips_only_the_row_checks():
+    """Both new-row pointers NULL: a step without new tokens (the row strides
+    are not checked); one of them NULL is refused.  The decode_write entry
+    needs both."""
+    assert _decode_step(0x300000, None) == -1
+    assert "new key/value" in P.lib.pkv_last_error().decode()
+    assert _decode_step(None, 0x400000) == -1
+    assert "new key/value" in P.lib.pkv_last_error().decode()
+    # both NULL, strides meaningless: the next failure is the decode's own
+    assert _decode_step(None, None, ks=0, vs=3, out=None) == -1
+    err = P.lib.pkv_last_error().decode()
+    assert "new key/value" not in err and "stride" not in err, err
+    assert _decode_write(nk=None, nv=None) == -1
+    assert "new key/value" in P.lib.pkv_last_error().decode()
+
+
 def test_wrappers_refuse_index_arrays_that_are_not_int32_device_tensors():
     """Block tables, lengths, launch orders, query starts and member lists
     reach the kernels as raw addresses; the binding refuses host tensors,

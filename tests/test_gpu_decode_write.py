@@ -143,11 +143,12 @@ def test_fused_write_zero_context_and_launch_order(decode_path):
     assert_close(OA.widen(got, s.dtype), ref, s.dtype, "fused, zero context, ordered")
 
 
-def _run_step(s, wl, tables, ctx, kc, vc, part, nbytes, seed, order=None):
-    """pkv_paged_attention_decode_step with a seeded pinned source of nbytes."""
+def _run_step(s, wl, tables, ctx, kc, vc, part, nbytes, seed, order=None, rows=True):
+    """pkv_paged_attention_decode_step with a seeded pinned source of nbytes
+    (rows=False: a step without new tokens, both new-row arguments None)."""
     kd, vd = to_dev(kc, s.dtype), to_dev(vc, s.dtype)
     q = to_dev(wl.q, s.dtype)
-    nk, nv = to_dev(wl.new_k, s.dtype), to_dev(wl.new_v, s.dtype)
+    nk, nv = (to_dev(wl.new_k, s.dtype), to_dev(wl.new_v, s.dtype)) if rows else (None, None)
     out = torch.empty_like(q)
     mx = int(ctx.max())
     wsb = P.decode_workspace_bytes(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim,
@@ -187,6 +188,34 @@ def test_decode_step_uploads_the_next_arrays_in_the_same_launch(name, part, deco
             assert np.array_equal(_bits(kd), _bits(ko)) and np.array_equal(_bits(vd), _bits(vo))
             fused, _, _ = _run(s, wl, tables, ctx, kc, vc, part, True, order=order)
             assert np.array_equal(_bits(got), _bits(fused)), "decode step vs fused write"
+            assert_close(OA.widen(got, s.dtype), ref, s.dtype, f"step {name} p{part} path{path}")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama7b", "gqa_prefix", "long_splitk",
+                                  "groups_g8_d64"])
+@pytest.mark.parametrize("part", [0, P.PARTITION_AUTO])
+def test_decode_step_without_new_tokens_uploads_and_decodes(name, part, decode_path):
+    """A step whose caches already hold every token: the decode step with no
+    new rows leaves the caches as they are, uploads the next arrays exactly,
+    and gives the output of paged_attention_decode bit for bit."""
+    s = CASES[name]
+    wl, slots, tables, ctx, kc, vc = _setup(s)
+    ko, vo = OC.reshape_and_cache(wl.new_k, wl.new_v, kc, vc, slots)
+    ref = OA.paged_decode(wl.q, ko, vo, tables, ctx, s.scale, s.dtype)
+    order = P.longest_first_order(ctx)
+    paths = [P.PATH_AUTO] if s.dtype == "f32" else [P.PATH_VALU, P.PATH_MFMA]
+    for path in paths:
+        decode_path(path)
+        for nbytes in (16, 16 * 40963):
+            log(f"decode step without new tokens {name} partition={part} path={path} "
+                f"upload={nbytes} B")
+            got, kd, vd, dst, src = _run_step(s, wl, tables, ctx, ko, vo, part, nbytes,
+                                              seed=nbytes + 1, order=order, rows=False)
+            assert np.array_equal(dst, src), "the next step's arrays"
+            assert np.array_equal(_bits(kd), _bits(ko)) and np.array_equal(_bits(vd), _bits(vo))
+            # the plain decode over the same caches (re-writing the rows they hold)
+            plain, _, _ = _run(s, wl, tables, ctx, ko, vo, part, False, order=order)
+            assert np.array_equal(_bits(got), _bits(plain)), "decode step vs plain decode"
             assert_close(OA.widen(got, s.dtype), ref, s.dtype, f"step {name} p{part} path{path}")
 
 

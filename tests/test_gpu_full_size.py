@@ -4,9 +4,10 @@ output row.
 Each test sets up the first timed step of ``bench.py --shape i`` the way the
 benchmark does: the pool sized with the benchmark's growth room, tables
 padded to the width of the last step, the longest-first launch order from
-the allocator, automatic partitioning, and for the LLaMA-13B batch the
-decode step that also writes the step's new tokens and uploads the next
-step's arrays.  The product allocator's
+the allocator, automatic partitioning, and the decode step that also
+uploads the next step's arrays (on the LLaMA-13B batch it also writes the
+step's new tokens; the shared-prefix call uploads nothing).  The product
+allocator's
 slots, tables, lengths and order must equal the oracle allocator's (and a
 stable longest-first sort) bit for bit; then every (sequence, query head)
 row of every launch is compared with the fp64 oracle
@@ -161,13 +162,42 @@ def _bits(a: np.ndarray) -> np.ndarray:
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
+def _stage(slots, tables, ctx):
+    """One step's arrays as the benchmark stages them: slots int64 |
+    tables int32 | lengths int32 | longest-first order int32, zero-padded
+    to 16 bytes (batches without new tokens leave the slots zero)."""
+    parts = [slots.view(np.uint8), tables.view(np.uint8).ravel(), ctx.view(np.uint8),
+             _longest_first(ctx).view(np.uint8)]
+    buf = np.concatenate(parts)
+    return np.concatenate([buf, np.zeros((-len(buf)) % 16, np.uint8)])
+
+
+def _decode_step_no_rows(st, d, part):
+    """The benchmark's call on a batch without new tokens: the decode and, in
+    the same launch, the upload of the next step's arrays (the same tables
+    again); the uploaded bytes must be exact."""
+    s = st.s
+    nxt = _stage(np.zeros(s.num_seqs, np.int64), st.tables, st.ctx.astype(np.int32))
+    src = torch.from_numpy(nxt).pin_memory()
+    dst = torch.zeros(len(nxt), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d.q)
+    P.paged_attention_decode_step(out, d.q, None, None, d.k, d.v, d.tables, d.ctx, d.max_ctx,
+                                  s.scale, dst, src, part, d.workspace(s, part),
+                                  seq_order=d.order)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), nxt), "the next step's arrays"
+    return OA.widen(from_dev(out, s.dtype), s.dtype)
+
+
 @pytest.mark.parametrize("idx", [0, 1])
 def test_full_tiny_and_llama7b(idx):
     st = bench_first_step(idx)
     log(f"full size {st.s.name}: B={st.s.num_seqs}, automatic partitioning, longest first")
     ref = _oracle(st)
     d = Dev(st, write=False)
-    assert_close(_decode(st, d, P.PARTITION_AUTO), ref, st.s.dtype, f"{st.s.name} full, AUTO")
+    got = _decode_step_no_rows(st, d, P.PARTITION_AUTO)
+    assert_close(got, ref, st.s.dtype, f"{st.s.name} full, decode step, AUTO")
+    np.testing.assert_array_equal(_decode(st, d, P.PARTITION_AUTO), got)
 
 
 def _next_step_arrays(st):
@@ -182,10 +212,7 @@ def _next_step_arrays(st):
         o.append(b, 1)
     slots = np.array([o.append(b, 1)[0] for b in range(B)], dtype=np.int64)
     tables, ctx = o.build_block_tables(list(range(B)), st.tables.shape[1], pad=-1)
-    parts = [slots.view(np.uint8), tables.view(np.uint8).ravel(), ctx.view(np.uint8),
-             _longest_first(ctx).view(np.uint8)]
-    buf = np.concatenate(parts)
-    return np.concatenate([buf, np.zeros((-len(buf)) % 16, np.uint8)])
+    return _stage(slots, tables, ctx)
 
 
 def test_full_llama13b_decode_step():
@@ -233,7 +260,9 @@ def test_full_gqa_prefix():
     log(f"full size {s.name}: B={s.num_seqs}, AUTO and shared prefix")
     ref = _oracle(st)
     d = Dev(st, write=False)
-    assert_close(_decode(st, d, P.PARTITION_AUTO), ref, s.dtype, f"{s.name} full, AUTO")
+    got = _decode_step_no_rows(st, d, P.PARTITION_AUTO)
+    assert_close(got, ref, s.dtype, f"{s.name} full, decode step, AUTO")
+    np.testing.assert_array_equal(_decode(st, d, P.PARTITION_AUTO), got)
     flag = np.zeros(s.num_seqs, dtype=np.int32)
     flag[st.members] = 1
     members = torch.from_numpy(st.members).cuda()
@@ -256,8 +285,10 @@ def test_full_long_splitk():
     log(f"full size {s.name}: B={s.num_seqs}, AUTO and 512-token partitions")
     ref = _oracle(st)
     d = Dev(st, write=False)
-    assert_close(_decode(st, d, P.PARTITION_AUTO), ref, s.dtype, f"{s.name} full, AUTO")
-    assert_close(_decode(st, d, 512), ref, s.dtype, f"{s.name} full, 512-token partitions")
+    for part in (P.PARTITION_AUTO, 512):
+        got = _decode_step_no_rows(st, d, part)
+        assert_close(got, ref, s.dtype, f"{s.name} full, decode step, partition {part}")
+        np.testing.assert_array_equal(_decode(st, d, part), got)
 
 
 def test_full_prefill_chunk():
