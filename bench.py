@@ -215,7 +215,10 @@ def summarize_counters(fetch_prefix: str, write_prefix: str, last: int, out_json
            "fetch_bytes_raw": int(fetch_b), "write_bytes_raw": int(write_b),
            "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
            "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4),
-           "steps": bench["steps"], "warmup": bench["warmup"]}
+           "steps": bench["steps"], "warmup": bench["warmup"],
+           # the launch configuration the counters were taken on
+           "partition_size": bench["config"]["partition_size"],
+           "upload": bench["config"].get("upload")}
     with open(out_json, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -855,8 +858,12 @@ def main() -> int:
             "algorithmic_bytes_all_timed_launches": int(np.mean(alg_bytes[timed])),
         }
         res["prefill_tokens_per_s"] = round(rows * K / elapsed, 1)
-    # (counters are recorded for the ordinary decode path only)
+    # (counters are recorded for the ordinary decode path only, and apply
+    # only to the partitioning and upload placement they were taken with)
     tr = None if shared else load_traffic(s.name, args.path, "prefill" if chunk else "decode")
+    if tr is not None and (tr.get("partition_size") != part_used
+                           or (not chunk and tr.get("upload") != res["config"]["upload"])):
+        tr = None
     if tr is not None and tr["steps"] == args.steps and tr["warmup"] == args.warmup:
         res["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
     elif tr is not None:
