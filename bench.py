@@ -51,10 +51,10 @@ def _args():
                     help="upload each step's tables on the compute stream instead of a side "
                          "stream overlapped with the previous step's attention")
     ap.add_argument("--upload-kernel", action="store_true",
-                    help="decode steps (not the shared-prefix call): upload each step's tables "
-                         "with their own upload launch (side stream, or --serial-upload) instead "
-                         "of within the previous step's decode launch "
-                         "(paged_attention_decode_step)")
+                    help="decode steps: upload each step's tables with their own upload launch "
+                         "(side stream, or --serial-upload) instead of within the previous step's "
+                         "decode launch (paged_attention_decode_step / "
+                         "paged_attention_decode_shared_prefix_step)")
     ap.add_argument("--staging-depth", type=int, default=8,
                     help="pinned staging buffers in flight (steps the host may run ahead)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
@@ -499,11 +499,10 @@ def main() -> int:
     chunk = s.chunk  # > 0: a chunked-prefill step of this many tokens per sequence
     step_tok = chunk if chunk else step_new  # tokens each sequence gains per step
     # decode steps with new tokens write them inside the decode launch, and
-    # (unless --upload-kernel) every decode launch but the shared-prefix one
-    # also uploads the next step's tables, which the host prepares one step
-    # ahead
+    # (unless --upload-kernel) every decode launch also uploads the next
+    # step's tables, which the host prepares one step ahead
     fused_write = bool(step_new) and not s.chunk and not args.separate_write
-    in_step = ((fused_write or not (step_new or s.chunk or args.shared_prefix))
+    in_step = ((fused_write or not (step_new or s.chunk))
                and not args.upload_kernel and not args.serial_upload)
     # growth room: in_step prepares one step more than it decodes
     wl = W.make_workload(s, extra_tokens=(total_steps + int(in_step)) * step_tok)
@@ -736,11 +735,17 @@ def main() -> int:
         _, d_tables, d_ctx, d_order = d_views[ds]
         if i in ev:
             ev[i][0].record(stream)
-        nk, nv = (new_k_steps[i], new_v_steps[i]) if step_new else (None, None)
-        P.paged_attention_decode_step(out, q, nk, nv, k_cache, v_cache,
-                                      d_tables, d_ctx, maxc, s.scale, d_stages[1 - ds],
-                                      h_stage[(i + 1) % nbuf], args.partition, workspace,
-                                      seq_order=d_order if use_order else None)
+        if shared:
+            P.paged_attention_decode_shared_prefix_step(
+                out, q, k_cache, v_cache, d_tables, d_ctx, maxc, s.scale, d_members,
+                d_member_flag, s.shared_prefix_tokens, d_stages[1 - ds], h_stage[(i + 1) % nbuf],
+                workspace, seq_order=d_order if use_order else None)
+        else:
+            nk, nv = (new_k_steps[i], new_v_steps[i]) if step_new else (None, None)
+            P.paged_attention_decode_step(out, q, nk, nv, k_cache, v_cache,
+                                          d_tables, d_ctx, maxc, s.scale, d_stages[1 - ds],
+                                          h_stage[(i + 1) % nbuf], args.partition, workspace,
+                                          seq_order=d_order if use_order else None)
         if i in ev:
             ev[i][1].record(stream)
         copied[(i + 1) % nbuf].record(stream)
@@ -820,6 +825,7 @@ def main() -> int:
         "roofline": {
             "kernel": ("paged_attention_decode"
                        + ("_step (cache write and next upload fused)" if in_step and fused_write
+                          else "_shared_prefix_step (next upload fused)" if in_step and shared
                           else "_step (next upload fused)" if in_step
                           else "_write (cache write fused)" if fused_write else "")
                        + (" (single pass)" if part_used == 0 else

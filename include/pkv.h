@@ -285,6 +285,27 @@ pkv_status pkv_paged_attention_decode_shared_prefix(
     int32_t prefix_tokens, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
     void* stream);
 
+/* pkv_paged_attention_decode_shared_prefix and, in the same launch, the
+ * next step's upload of pkv_paged_attention_decode_step: next_bytes from
+ * next_src_host (pinned, device-mapped host memory) to next_dst (device) by
+ * the workgroups of one extra grid row dispatched before the prefix tiles
+ * ("vLLM in Production …", section "Continuous Batching Keeps the GPU
+ * Full": the batch is re-formed at every step).  next_dst must not overlap
+ * anything the call reads or writes; next_src_host must not change until
+ * the call has completed.  next_bytes = 0: exactly the shared-prefix call.
+ * next_bytes and both addresses must be multiples of 16, the batch 1 ..
+ * 65534 sequences; PKV_ERR_INVALID_ARG (nothing launched) otherwise or if
+ * the source is not pinned, mapped host memory.  Other arguments and errors
+ * as pkv_paged_attention_decode_shared_prefix. */
+pkv_status pkv_paged_attention_decode_shared_prefix_step(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    const int32_t* members, const int32_t* member_flag, int32_t num_members,
+    int32_t prefix_tokens, void* workspace, size_t workspace_bytes, void* next_dst,
+    const void* next_src_host, size_t next_bytes, pkv_dtype dtype, void* stream);
+
 /* The decode step in one launch (the cache write fused into the attention):
  * for every sequence b with context_lens[b] > 0, its new token is its last
  * position p = context_lens[b] - 1 (already appended by the allocator), and

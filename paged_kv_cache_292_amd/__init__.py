@@ -26,6 +26,7 @@ __all__ = [
     "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "Allocator", "EXPORTS", "version",
     "blocks_for_budget", "validate_decode_inputs", "paged_attention_decode_noalloc",
     "NOALLOC_SCRATCH_BYTES", "paged_attention_decode_step",
+    "paged_attention_decode_shared_prefix_step",
 ]
 
 LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
@@ -64,6 +65,9 @@ EXPORTS = {
                                                         _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                         _f32, _vp, _vp, _i32, _i32, _vp, _sz,
                                                         _i32, _vp]),
+    "pkv_paged_attention_decode_shared_prefix_step": (
+        _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+               _f32, _vp, _vp, _i32, _i32, _vp, _sz, _vp, _vp, _sz, _i32, _vp]),
     "pkv_paged_attention_decode_write": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
                                                 _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
@@ -349,6 +353,18 @@ def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, conte
         dt, _stream_ptr(stream)), fn)
 
 
+def _next_upload(next_dst, next_src_pinned, fn):
+    """Pointers and byte count of the next step's upload (a contiguous device
+    tensor and a contiguous pinned host tensor of the same byte size)."""
+    nbytes = next_src_pinned.numel() * next_src_pinned.element_size()
+    if (next_dst.numel() * next_dst.element_size() != nbytes or not next_dst.is_cuda
+            or not next_dst.is_contiguous() or next_src_pinned.is_cuda
+            or not next_src_pinned.is_contiguous()):
+        raise ValueError(f"{fn}: next_dst must be a contiguous device tensor and "
+                         "next_src_pinned a contiguous pinned host tensor of the same byte size")
+    return next_dst.data_ptr(), next_src_pinned.data_ptr(), nbytes
+
+
 def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens,
                                          max_context_len: int, scale: float, members,
                                          member_flag, prefix_tokens: int, workspace=None,
@@ -359,7 +375,29 @@ def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
     the same blocks) is computed once per tile of members.
     ``member_flag``: device int32 [num_seqs], nonzero for the members;
     ``workspace``: at least ``decode_workspace_bytes(..., prefix_tokens)``."""
-    fn = "paged_attention_decode_shared_prefix"
+    _shared_prefix("paged_attention_decode_shared_prefix", out, q, k_cache, v_cache,
+                   block_tables, context_lens, max_context_len, scale, members, member_flag,
+                   prefix_tokens, workspace, stream, seq_order, None)
+
+
+def paged_attention_decode_shared_prefix_step(out, q, k_cache, v_cache, block_tables,
+                                              context_lens, max_context_len: int, scale: float,
+                                              members, member_flag, prefix_tokens: int,
+                                              next_dst, next_src_pinned, workspace=None,
+                                              stream=None, seq_order=None) -> None:
+    """``paged_attention_decode_shared_prefix`` and, in the same launch, a
+    copy of the pinned host tensor ``next_src_pinned`` into the device
+    tensor ``next_dst`` (the next step's index arrays; equal byte sizes,
+    multiples of 16)."""
+    fn = "paged_attention_decode_shared_prefix_step"
+    _shared_prefix(fn, out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                   scale, members, member_flag, prefix_tokens, workspace, stream, seq_order,
+                   _next_upload(next_dst, next_src_pinned, fn))
+
+
+def _shared_prefix(fn, out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                   scale, members, member_flag, prefix_tokens, workspace, stream, seq_order,
+                   upload):
     B, Hq = q.shape[0], q.shape[1]
     idx = _decode_indices(block_tables, context_lens, seq_order, B, fn)
     M = members.numel() if members is not None else 0
@@ -368,10 +406,14 @@ def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
     (N, bs, Hkv, D), dt = _caches(k_cache, v_cache, fn)
     qp, op = _q_out(q, out, (B, Hq, D), k_cache.dtype, fn)
     ws_ptr, ws_bytes = _workspace(workspace, fn)
-    _check(lib.pkv_paged_attention_decode_shared_prefix(
-        op, qp, k_cache.data_ptr(), v_cache.data_ptr(), idx[0], block_tables.shape[1], idx[1],
-        idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), mp, fp, M,
-        int(prefix_tokens), ws_ptr, ws_bytes, dt, _stream_ptr(stream)), fn)
+    common = (op, qp, k_cache.data_ptr(), v_cache.data_ptr(), idx[0], block_tables.shape[1],
+              idx[1], idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N, float(scale), mp, fp, M,
+              int(prefix_tokens), ws_ptr, ws_bytes)
+    if upload is None:
+        _check(lib.pkv_paged_attention_decode_shared_prefix(*common, dt, _stream_ptr(stream)), fn)
+    else:
+        _check(lib.pkv_paged_attention_decode_shared_prefix_step(
+            *common, *upload, dt, _stream_ptr(stream)), fn)
 
 
 def paged_attention_decode_write(out, q, new_key, new_value, k_cache, v_cache, block_tables,
@@ -421,18 +463,13 @@ def paged_attention_decode_step(out, q, new_key, new_value, k_cache, v_cache, bl
         vp = _dense_ptr(new_value, (B, Hkv, D), k_cache.dtype, "new_value", fn, rows=True)
         ks = new_key.stride(0) if B else Hkv * D
         vs = new_value.stride(0) if B else Hkv * D
-    nbytes = next_src_pinned.numel() * next_src_pinned.element_size()
-    if (next_dst.numel() * next_dst.element_size() != nbytes or not next_dst.is_cuda
-            or not next_dst.is_contiguous() or next_src_pinned.is_cuda
-            or not next_src_pinned.is_contiguous()):
-        raise ValueError(f"{fn}: next_dst must be a contiguous device tensor and "
-                         "next_src_pinned a contiguous pinned host tensor of the same byte size")
+    nd, ns, nbytes = _next_upload(next_dst, next_src_pinned, fn)
     ws_ptr, ws_bytes = _workspace(workspace, fn)
     _check(lib.pkv_paged_attention_decode_step(
         op, qp, kp, vp, ks, vs, k_cache.data_ptr(), v_cache.data_ptr(), idx[0],
         block_tables.shape[1], idx[1], idx[2], int(max_context_len), B, Hq, Hkv, D, bs, N,
-        float(scale), int(partition_size), ws_ptr, ws_bytes, next_dst.data_ptr(),
-        next_src_pinned.data_ptr(), nbytes, dt, _stream_ptr(stream)), fn)
+        float(scale), int(partition_size), ws_ptr, ws_bytes, nd, ns, nbytes, dt,
+        _stream_ptr(stream)), fn)
 
 
 def upload_pinned(dst, src_pinned, stream=None) -> None:

@@ -447,7 +447,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
-  if (int(blockIdx.z) < w.pf_rows) {  // the next step's upload (never with shared-prefix rows)
+  if (int(blockIdx.z) < w.pf_rows) {  // the next step's upload
     copy_next_step(w);
     return;
   }
@@ -455,8 +455,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   // Shared-prefix rows: a tile of 16 / G members sharing the prefix; its
   // operand columns are (member, query head) pairs, and it computes the
   // members' partition 0 (the prefix) with one read of the prefix's K/V.
-  // Grid rows: the sequences' rows from seq_z0, the tiles' rows from
-  // group_z0 to group_z1.
+  // Grid rows: the upload's first, then the tiles' from group_z0 to
+  // group_z1, then the sequences' from seq_z0 + pf_rows.
   const bool group = !WRITE && a.members != nullptr && int(blockIdx.z) >= a.group_z0 &&
                      int(blockIdx.z) < a.group_z1;
   // The tiles' workgroups in launch order: workgroup w takes kv head
@@ -886,9 +886,11 @@ hipError_t launch_mfma(const AttnArgs& a, const NewRows& w, int num_seqs, hipStr
       const int mpg = 16 / (a.num_q_heads / a.num_kv_heads);
       const int tiles = (a.num_members + mpg - 1) / mpg;
       const int rows = (tiles + int(grid.x) - 1) / int(grid.x);
-      ag.group_z0 = 0;  // first: the tiles read the prefix while the rest starts
-      ag.group_z1 = rows;
-      ag.seq_z0 = rows;
+      // first (after the next step's upload row, if any): the tiles read the
+      // prefix while the rest starts
+      ag.group_z0 = w.pf_rows;
+      ag.group_z1 = w.pf_rows + rows;
+      ag.seq_z0 = rows;  // the sequences' rows follow the upload row and the tiles
       grid.z += unsigned(rows);
     }
     hipLaunchKernelGGL((decode_mfma_kernel<D, BS, kNW, 1, WRITE>), grid, dim3(kNW * 64), 0, st, ag,
@@ -1172,15 +1174,46 @@ extern "C" pkv_status pkv_paged_attention_decode(
                      partition_size, workspace, workspace_bytes, dtype, stream, nullptr);
 }
 
-extern "C" pkv_status pkv_paged_attention_decode_shared_prefix(
-    void* out, const void* q, const void* k_cache, const void* v_cache,
-    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-    const int32_t* members, const int32_t* member_flag, int32_t num_members,
-    int32_t prefix_tokens, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-    void* stream) {
-  const char* fn = "paged_attention_decode_shared_prefix";
+namespace {
+
+// The next step's upload within a decode launch: checks the buffers and
+// fills w's upload fields (one more grid row of workgroups, dispatched
+// first).  next_bytes = 0: no upload.
+pkv_status next_step_upload(const char* fn, void* next_dst, const void* next_src_host,
+                            size_t next_bytes, int32_t num_seqs, pkv::NewRows& w) {
+  if (next_bytes == 0) return pkv::ok();
+  if (!next_dst || !next_src_host || next_bytes % 16 ||
+      (reinterpret_cast<uintptr_t>(next_dst) & 15u) ||
+      (reinterpret_cast<uintptr_t>(next_src_host) & 15u))
+    return fail(PKV_ERR_INVALID_ARG,
+                "%s: the next step's upload needs non-NULL 16-byte aligned buffers and a "
+                "multiple of 16 bytes (%zu)", fn, next_bytes);
+  if (num_seqs <= 0 || num_seqs > 65534)
+    return fail(PKV_ERR_INVALID_ARG,
+                "%s: the next step's upload needs 1 .. 65534 sequences (its grid row comes "
+                "first), got %d", fn, num_seqs);
+  void* src_dev = pkv::mapped_host(const_cast<void*>(next_src_host));
+  if (!src_dev)
+    return fail(PKV_ERR_INVALID_ARG, "%s: next_src_host is not pinned, device-mapped host memory",
+                fn);
+  w.pf_src = static_cast<const uint4*>(src_dev);
+  w.pf_dst = static_cast<uint4*>(next_dst);
+  w.pf_n16 = int64_t(next_bytes / 16);
+  w.pf_rows = 1;
+  return pkv::ok();
+}
+
+// The shared-prefix decode, optionally with the next step's upload.
+pkv_status shared_prefix_call(const char* fn, void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              const int32_t* seq_order, int32_t max_context_len,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              float scale, const int32_t* members, const int32_t* member_flag,
+                              int32_t num_members, int32_t prefix_tokens, void* workspace,
+                              size_t workspace_bytes, void* next_dst, const void* next_src_host,
+                              size_t next_bytes, pkv_dtype dtype, void* stream) {
   if (dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "%s: bf16 only", fn);
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
@@ -1194,7 +1227,8 @@ extern "C" pkv_status pkv_paged_attention_decode_shared_prefix(
   if (num_members > 0 && (!members || !member_flag))
     return fail(PKV_ERR_INVALID_ARG, "%s: NULL members or member_flag", fn);
   const int32_t mpg = 16 / (num_q_heads / num_kv_heads);
-  if (int64_t(num_seqs) + (int64_t(num_members) + mpg - 1) / mpg > 65535)
+  const int64_t upload_rows = next_bytes > 0 ? 1 : 0;
+  if (int64_t(num_seqs) + (int64_t(num_members) + mpg - 1) / mpg + upload_rows > 65535)
     return fail(PKV_ERR_INVALID_ARG, "%s: %d sequences and %d members exceed the grid", fn,
                 num_seqs, num_members);
   if (prefix_tokens <= 0 || block_size <= 0 || prefix_tokens % block_size != 0 ||
@@ -1203,11 +1237,48 @@ extern "C" pkv_status pkv_paged_attention_decode_shared_prefix(
                 "%s: prefix_tokens=%d must be a positive multiple of block_size=%d and of %d, "
                 "at most max_context_len=%d", fn, prefix_tokens, block_size, pkv::kChunk,
                 max_context_len);
+  pkv::NewRows w{};
+  const pkv_status st = next_step_upload(fn, next_dst, next_src_host, next_bytes, num_seqs, w);
+  if (st != PKV_OK) return st;
   return decode_call(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, seq_order, max_context_len, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, prefix_tokens,
                      workspace, workspace_bytes, dtype, stream, nullptr, members, member_flag,
-                     num_members);
+                     num_members, &w);
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attention_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    const int32_t* members, const int32_t* member_flag, int32_t num_members,
+    int32_t prefix_tokens, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+    void* stream) {
+  return shared_prefix_call("paged_attention_decode_shared_prefix", out, q, k_cache, v_cache,
+                            block_tables, max_blocks_per_seq, context_lens, seq_order,
+                            max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, num_blocks, scale, members, member_flag, num_members,
+                            prefix_tokens, workspace, workspace_bytes, nullptr, nullptr, 0, dtype,
+                            stream);
+}
+
+extern "C" pkv_status pkv_paged_attention_decode_shared_prefix_step(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* seq_order, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    const int32_t* members, const int32_t* member_flag, int32_t num_members,
+    int32_t prefix_tokens, void* workspace, size_t workspace_bytes, void* next_dst,
+    const void* next_src_host, size_t next_bytes, pkv_dtype dtype, void* stream) {
+  return shared_prefix_call("paged_attention_decode_shared_prefix_step", out, q, k_cache,
+                            v_cache, block_tables, max_blocks_per_seq, context_lens, seq_order,
+                            max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, num_blocks, scale, members, member_flag, num_members,
+                            prefix_tokens, workspace, workspace_bytes, next_dst, next_src_host,
+                            next_bytes, dtype, stream);
 }
 
 namespace {
@@ -1216,8 +1287,8 @@ namespace {
 // upload, in one launch: the checks of both entry points.  rows_optional:
 // new_key and new_value both NULL mean a step without new tokens (no cache
 // write, the attention of pkv_paged_attention_decode).
-pkv_status decode_write_call(const char* fn, bool rows_optional, void* out, const void* q, const void* new_key,
-                             const void* new_value, int64_t key_seq_stride,
+pkv_status decode_write_call(const char* fn, bool rows_optional, void* out, const void* q,
+                             const void* new_key, const void* new_value, int64_t key_seq_stride,
                              int64_t value_seq_stride, void* k_cache, void* v_cache,
                              const int32_t* block_tables, int32_t max_blocks_per_seq,
                              const int32_t* context_lens, const int32_t* seq_order,
@@ -1241,26 +1312,8 @@ pkv_status decode_write_call(const char* fn, bool rows_optional, void* out, cons
                 "elements and multiples of 16 bytes, pointers 16-byte aligned", fn,
                 (long long)key_seq_stride, (long long)value_seq_stride, (long long)row);
   pkv::NewRows w{new_key, new_value, key_seq_stride, value_seq_stride, nullptr, nullptr, 0, 0};
-  if (next_bytes > 0) {
-    if (!next_dst || !next_src_host || next_bytes % 16 ||
-        (reinterpret_cast<uintptr_t>(next_dst) & 15u) ||
-        (reinterpret_cast<uintptr_t>(next_src_host) & 15u))
-      return fail(PKV_ERR_INVALID_ARG,
-                  "%s: the next step's upload needs non-NULL 16-byte aligned buffers and a "
-                  "multiple of 16 bytes (%zu)", fn, next_bytes);
-    void* src_dev = pkv::mapped_host(const_cast<void*>(next_src_host));
-    if (!src_dev)
-      return fail(PKV_ERR_INVALID_ARG, "%s: next_src_host is not pinned, device-mapped host memory",
-                  fn);
-    w.pf_src = static_cast<const uint4*>(src_dev);
-    w.pf_dst = static_cast<uint4*>(next_dst);
-    w.pf_n16 = int64_t(next_bytes / 16);
-    w.pf_rows = 1;
-    if (num_seqs == 0 || num_seqs > 65534)
-      return fail(PKV_ERR_INVALID_ARG,
-                  "%s: the next step's upload needs 1 .. 65534 sequences (its grid row comes "
-                  "first), got %d", fn, num_seqs);
-  }
+  const pkv_status st = next_step_upload(fn, next_dst, next_src_host, next_bytes, num_seqs, w);
+  if (st != PKV_OK) return st;
   return decode_call(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, seq_order, max_context_len, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size,

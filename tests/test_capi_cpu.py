@@ -427,6 +427,24 @@ def test_decode_step_without_new_rows_skips_only_the_row_checks():
     assert "new key/value" in P.lib.pkv_last_error().decode()
 
 
+def test_shared_prefix_step_refuses_a_bad_upload_before_launch():
+    """The upload's checks come before anything touches the GPU: sizes and
+    alignment, and a batch for its grid row."""
+    def call(next_dst, next_src, nbytes, B=4, M=2):
+        return P.lib.pkv_paged_attention_decode_shared_prefix_step(
+            0x100000, 0x200000, 0x500000, 0x600000, 0x700000, 4, 0x800000, None, 64, B, 32, 8,
+            128, 16, 8, 0.1, 0x900000, 0xa00000, M, 16, 0xb00000, 1 << 20, next_dst, next_src,
+            nbytes, P.BF16, None)
+    assert call(0x1000, 0x2000, 24) == -1              # not a multiple of 16
+    assert "next step's upload" in P.lib.pkv_last_error().decode()
+    assert call(0x1008, 0x2000, 32) == -1              # misaligned destination
+    assert call(None, 0x2000, 32) == -1
+    assert call(0x1000, 0x2000, 32, B=0, M=0) == -1    # no sequence for the grid row
+    assert "1 .. 65534" in P.lib.pkv_last_error().decode()
+    assert call(0x1000, 0x2000, 32, B=65535) == -1     # the grid limit with the upload row
+    assert "exceed the grid" in P.lib.pkv_last_error().decode()
+
+
 def test_wrappers_refuse_index_arrays_that_are_not_int32_device_tensors():
     """Block tables, lengths, launch orders, query starts and member lists
     reach the kernels as raw addresses; the binding refuses host tensors,

@@ -6,10 +6,9 @@ benchmark does: the pool sized with the benchmark's growth room, tables
 padded to the width of the last step, the longest-first launch order from
 the allocator, automatic partitioning, and the decode step that also
 uploads the next step's arrays (on the LLaMA-13B batch it also writes the
-step's new tokens; the shared-prefix call uploads nothing).  The product
-allocator's
-slots, tables, lengths and order must equal the oracle allocator's (and a
-stable longest-first sort) bit for bit; then every (sequence, query head)
+step's new tokens; the GQA batch also runs the shared-prefix step).  The
+product allocator's slots, tables, lengths and order must equal the oracle
+allocator's (and a stable longest-first sort) bit for bit; then every (sequence, query head)
 row of every launch is compared with the fp64 oracle
 (``oracle.attention.paged_decode``; chunked prefill: every query row of the
 longest, the shortest and one more sequence, all heads) at the bf16
@@ -273,8 +272,21 @@ def test_full_gqa_prefix():
                                            d.workspace(s, s.shared_prefix_tokens),
                                            seq_order=d.order)
     torch.cuda.synchronize()
-    assert_close(OA.widen(from_dev(out, s.dtype), s.dtype), ref, s.dtype,
-                 f"{s.name} full, shared prefix")
+    shared_out = OA.widen(from_dev(out, s.dtype), s.dtype)
+    assert_close(shared_out, ref, s.dtype, f"{s.name} full, shared prefix")
+    # the call bench.py --shared-prefix times: the same with the next upload
+    nxt = _stage(np.zeros(s.num_seqs, np.int64), st.tables, st.ctx.astype(np.int32))
+    src = torch.from_numpy(nxt).pin_memory()
+    dst = torch.zeros(len(nxt), dtype=torch.uint8, device="cuda")
+    out2 = torch.empty_like(d.q)
+    P.paged_attention_decode_shared_prefix_step(out2, d.q, d.k, d.v, d.tables, d.ctx, d.max_ctx,
+                                                s.scale, members, torch.from_numpy(flag).cuda(),
+                                                s.shared_prefix_tokens, dst, src,
+                                                d.workspace(s, s.shared_prefix_tokens),
+                                                seq_order=d.order)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), nxt), "the next step's arrays"
+    np.testing.assert_array_equal(OA.widen(from_dev(out2, s.dtype), s.dtype), shared_out)
 
 
 def test_full_long_splitk():

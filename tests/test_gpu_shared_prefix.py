@@ -26,7 +26,9 @@ def decode_path():
     P.set_decode_path(P.PATH_AUTO)
 
 
-def run_shared(st, members, prefix, order=None):
+def run_shared(st, members, prefix, order=None, upload=None):
+    """The shared-prefix call; upload = (device dst, pinned src) runs the
+    step form that also copies src into dst within the launch."""
     s = st.shape
     out = torch.empty_like(st.q)
     ws_bytes = P.decode_workspace_bytes(s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim,
@@ -37,9 +39,15 @@ def run_shared(st, members, prefix, order=None):
     m_dev = torch.from_numpy(np.ascontiguousarray(members, dtype=np.int32)).cuda()
     f_dev = torch.from_numpy(flag).cuda()
     so = torch.from_numpy(np.ascontiguousarray(order, dtype=np.int32)).cuda() if order is not None else None
-    P.paged_attention_decode_shared_prefix(out, st.q, st.k_cache, st.v_cache, st.tables_dev,
-                                           st.ctx_dev, st.max_ctx, s.scale, m_dev, f_dev,
-                                           prefix, ws, seq_order=so)
+    if upload is None:
+        P.paged_attention_decode_shared_prefix(out, st.q, st.k_cache, st.v_cache, st.tables_dev,
+                                               st.ctx_dev, st.max_ctx, s.scale, m_dev, f_dev,
+                                               prefix, ws, seq_order=so)
+    else:
+        P.paged_attention_decode_shared_prefix_step(out, st.q, st.k_cache, st.v_cache,
+                                                    st.tables_dev, st.ctx_dev, st.max_ctx,
+                                                    s.scale, m_dev, f_dev, prefix, upload[0],
+                                                    upload[1], ws, seq_order=so)
     torch.cuda.synchronize()
     from gpu_cases import OA, from_dev
     return OA.widen(from_dev(out, s.dtype), s.dtype)
@@ -113,3 +121,33 @@ def test_shared_prefix_full_gqa_shape_sampled():
     pairs = [(int(b), h) for b in bs_ for h in (0, 13, s.num_q_heads - 1)]
     assert_close(np.stack([got[b, h] for b, h in pairs]), oracle_rows(st, pairs), "bf16",
                  "full GQA shared prefix")
+
+
+@pytest.mark.parametrize("B,hq,hkv,D,bs,prefix,sharers", [
+    (16, 32, 8, 128, 32, 1024, 6),
+    (12, 16, 2, 128, 16, 512, 9),
+    (9, 6, 2, 64, 16, 96, 8),
+])
+def test_shared_prefix_step_uploads_the_next_arrays_in_the_same_launch(B, hq, hkv, D, bs, prefix,
+                                                                      sharers, decode_path):
+    """The step form: output bit-identical to the shared-prefix call (the
+    same workgroups, shifted one grid row), the uploaded bytes exact, for an
+    upload of one piece and one larger than a grid row's threads."""
+    if hq // hkv < 4:
+        decode_path(P.PATH_MFMA)
+    s = shape_with_sharing(B, hq, hkv, D, bs, prefix, sharers, prefix + 1, prefix + 900,
+                           seed=hq * 37 + prefix)
+    st = build_step(s, poison=True, pad=-5)
+    members = st.wl.sharers
+    ref = oracle_full(st)
+    order = P.longest_first_order(st.ctx)
+    plain = run_shared(st, members, prefix, order)
+    for nbytes in (16, 16 * 40963):
+        log(f"shared prefix step G={hq // hkv} prefix={prefix} upload={nbytes} B")
+        src_np = np.random.default_rng(nbytes).integers(0, 256, nbytes, dtype=np.uint8)
+        src = torch.from_numpy(src_np).pin_memory()
+        dst = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+        got = run_shared(st, members, prefix, order, upload=(dst, src))
+        assert np.array_equal(dst.cpu().numpy(), src_np), "the next step's arrays"
+        np.testing.assert_array_equal(got, plain)
+        assert_close(got, ref, "bf16", f"shared prefix step G{hq // hkv}")
