@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from gpu_cases import assert_close, build_step, log, oracle_full, oracle_rows, run_decode
+from gpu_cases import OA, assert_close, build_step, from_dev, log, oracle_full, oracle_rows, run_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -194,3 +194,38 @@ def test_maximum_batch_and_context():
     ref = oracle_full(st2)
     for part in (0, 16, P.PARTITION_AUTO):
         assert_close(run_decode(st2, part), ref, "bf16", f"131089 tokens p{part}")
+
+
+def test_decode_step_at_the_largest_batch_with_an_upload():
+    """The decode step with the next step's upload takes one grid row more:
+    65,534 sequences is its largest batch (sampled rows vs the oracle, the
+    output bit-identical to the plain decode, the upload exact); at 65,535
+    it refuses before launching anything."""
+    s = W.DecodeShape("max_step", "bf16", 65534, 2, 1, 64, 16, "uniform", ctx_lo=1, ctx_hi=4,
+                      seed=93)
+    st = build_step(s, poison=True)
+    base = run_decode(st, P.PARTITION_AUTO)
+    nbytes = 16 * 4099
+    src_np = np.random.default_rng(94).integers(0, 256, nbytes, dtype=np.uint8)
+    src = torch.from_numpy(src_np).pin_memory()
+    dst = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(st.q)
+    log("decode step, 65534 sequences, no new tokens, upload")
+    P.paged_attention_decode_step(out, st.q, None, None, st.k_cache, st.v_cache, st.tables_dev,
+                                  st.ctx_dev, st.max_ctx, s.scale, dst, src)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), src_np), "the next step's arrays"
+    got = OA.widen(from_dev(out, s.dtype), s.dtype)
+    np.testing.assert_array_equal(got, base)
+    pairs = [(b, h) for b in (0, 1, 4095, 40000, 65533) for h in (0, 1)]
+    assert_close(np.stack([got[b, h] for b, h in pairs]), oracle_rows(st, pairs), "bf16",
+                 "65534 sequences, decode step")
+    s2 = W.DecodeShape("max_step_over", "bf16", 65535, 2, 1, 64, 16, "uniform", ctx_lo=1,
+                       ctx_hi=4, seed=95)
+    st2 = build_step(s2, poison=True)
+    out2 = torch.full_like(st2.q, 3.0)
+    with pytest.raises(P.PkvError, match="INVALID_ARG"):
+        P.paged_attention_decode_step(out2, st2.q, None, None, st2.k_cache, st2.v_cache,
+                                      st2.tables_dev, st2.ctx_dev, st2.max_ctx, s2.scale, dst, src)
+    torch.cuda.synchronize()
+    assert (out2.float() == 3.0).all()
