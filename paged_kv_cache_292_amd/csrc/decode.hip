@@ -460,17 +460,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
   const bool group = !WRITE && a.members != nullptr && int(blockIdx.z) >= a.group_z0 &&
                      int(blockIdx.z) < a.group_z1;
   // The tiles' workgroups in launch order: workgroup w takes kv head
-  // w % Hkv and tile w / Hkv, so with the kv heads in eights every tile of a
-  // kv head lands on the same XCD (workgroups are dealt to the 8 XCDs
-  // round-robin) and reads the prefix rows the others fetched into its L2.
+  // w % Hkv and tiles NW * (w / Hkv) .. + NW - 1, so with the kv heads in
+  // eights every tile of a kv head lands on the same XCD (workgroups are
+  // dealt to the 8 XCDs round-robin) and reads the prefix rows the others
+  // fetched into its L2.
   const int gw = group ? int(blockIdx.x) + int(gridDim.x) * (int(blockIdx.y) +
                                                              int(gridDim.y) * (int(blockIdx.z) - a.group_z0))
                        : 0;
   const int kvh0 = group ? gw % Hkv : int(blockIdx.y) * HG;  // first kv head
   const int kvh = kvh0 + wave % HG;  // this wave's kv head
-  const int stream = wave / HG;      // this wave's chunk stream
+  // A tiles' workgroup holds NW tiles of one kv head, one per wave, each
+  // wave over the whole prefix: its waves read the same rows, the later ones
+  // from L1 (measured on MI355X, GQA batch with 128 of 256 sequences sharing
+  // 1,024 tokens: 656.7-658.0 us against 663.3-665.5 with one tile per
+  // workgroup and its prefix split over the waves)
+  const int stream = group ? 0 : wave / HG;  // this wave's chunk stream
   const int mpg = 16 / G;  // members per tile
-  const int tile = group ? gw / Hkv : 0;
+  const int tile = group ? (gw / Hkv) * NW + wave : 0;
   const int tile_members = group ? min(mpg, a.num_members - tile * mpg) : 0;
   if (group && tile_members <= 0) return;
   auto member_seq = [&](int i) {
@@ -593,14 +599,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = !live ? 0u : (tc + 4 * c + i < t1l ? voff[i] : vmask);
       const char* vsrc = vb + off;
+      // the tiles' V loads are cached: the workgroup's other waves read them too
       if constexpr (VW == 4) {
-        const uint4 x = load16<kMfmaVNT>(vsrc);
+        const uint4 x = group ? load16<false>(vsrc) : load16<kMfmaVNT>(vsrc);
         r.v[i][0] = x.x;
         r.v[i][1] = x.y;
         r.v[i][2] = x.z;
         r.v[i][3] = x.w;
       } else {
-        const uint2 x = load8<kMfmaVNT>(vsrc);
+        const uint2 x = group ? load8<false>(vsrc) : load8<kMfmaVNT>(vsrc);
         r.v[i][0] = x.x;
         r.v[i][1] = x.y;
       }
@@ -654,7 +661,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
 
   auto consume = [&](int ch, const Regs& r) { consume_at(ch * kChunk, t1l, r); };
 
-  constexpr int WSTEP = S;  // chunks between one wave's iterations
+  const int WSTEP = group ? 1 : S;  // chunks between one wave's iterations
   Regs ra, rb;
   int ch = c_begin + stream;
   if (ch < c_end) {
@@ -723,7 +730,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a, NewRow
       }
     }
   };
-  if constexpr (S == 1) {  // this wave holds all of its rows' tokens
+  if (S == 1 || group) {  // this wave holds all of its rows' tokens
     if (row_ok) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -885,7 +892,8 @@ hipError_t launch_mfma(const AttnArgs& a, const NewRows& w, int num_seqs, hipStr
       // the tiles after the sequences)
       const int mpg = 16 / (a.num_q_heads / a.num_kv_heads);
       const int tiles = (a.num_members + mpg - 1) / mpg;
-      const int rows = (tiles + int(grid.x) - 1) / int(grid.x);
+      const int tile_wgs = (tiles + kNW - 1) / kNW;  // kNW tiles per workgroup
+      const int rows = (tile_wgs + int(grid.x) - 1) / int(grid.x);
       // first (after the next step's upload row, if any): the tiles read the
       // prefix while the rest starts
       ag.group_z0 = w.pf_rows;
