@@ -1,6 +1,6 @@
-"""The benchmark's command-line contract: one JSON line with the fields the
-round's tooling reads (metric, value, roofline, CPU baseline ...), and a
-clear refusal of more than one GPU."""
+"""The benchmark's command-line contract: one JSON line with its fixed set
+of fields (metric, value, roofline, CPU baseline ...), and a clear refusal
+of more than one GPU."""
 import json
 import os
 import subprocess
