@@ -60,8 +60,9 @@ def _args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="decode a batch with a shared prefix through "
-                         "paged_attention_decode_shared_prefix (the prefix partition computed "
-                         "once per tile of sharing sequences)")
+                         "paged_attention_decode_shared_prefix_step (the prefix partition "
+                         "computed once per tile of sharing sequences; "
+                         "paged_attention_decode_shared_prefix with --upload-kernel)")
     ap.add_argument("--prefix-tokens", type=int, default=None,
                     help="length of the shared prefix of a batch with sharing (the GQA batch: "
                          "1024 as specified); sharers are drawn among longer sequences")
@@ -235,6 +236,24 @@ def load_traffic(workload: str, path_name: str, kind: str):
     if rec.get("kernel_source_sha256") != kernel_source_hash(kind):
         return None
     return rec
+
+
+def traffic_for(rec, partition_size: int, upload: str, prefill: bool, steps: int, warmup: int,
+                alg_bytes: int):
+    """HBM traffic per launch for this run from a stored counter record
+    (``load_traffic``): None unless the record was taken with this run's
+    partition size and (decode) upload placement; the record's own figure
+    for the same step counts, else its traffic per algorithmic byte times
+    this run's algorithmic bytes (other step counts read other contexts).
+    Returns (traffic or None, note or None)."""
+    if rec is None or rec.get("partition_size") != partition_size:
+        return None, None
+    if not prefill and rec.get("upload") != upload:
+        return None, None
+    if rec["steps"] == steps and rec["warmup"] == warmup:
+        return rec["traffic_bytes_per_launch"], None
+    return (int(round(rec["traffic_over_algorithmic"] * alg_bytes)),
+            f"{rec['steps']}-step counter run, traffic/algorithmic {rec['traffic_over_algorithmic']}")
 
 
 HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, per direction, published
@@ -867,19 +886,12 @@ def main() -> int:
     # (counters are recorded for the ordinary decode path only, and apply
     # only to the partitioning and upload placement they were taken with)
     tr = None if shared else load_traffic(s.name, args.path, "prefill" if chunk else "decode")
-    if tr is not None and (tr.get("partition_size") != part_used
-                           or (not chunk and tr.get("upload") != res["config"]["upload"])):
-        tr = None
-    if tr is not None and tr["steps"] == args.steps and tr["warmup"] == args.warmup:
-        res["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
-    elif tr is not None:
-        # other step counts change the contexts the launches read: the
-        # counter run's traffic per algorithmic byte, applied to this run's
-        # algorithmic bytes per launch
-        res["roofline"]["traffic"] = int(round(tr["traffic_over_algorithmic"]
-                                               * res["roofline"]["algorithmic_bytes_per_launch"]))
-        res["roofline"]["traffic_scaled_from"] = (
-            f"{tr['steps']}-step counter run, traffic/algorithmic {tr['traffic_over_algorithmic']}")
+    traffic, scaled_from = traffic_for(tr, part_used, res["config"]["upload"], bool(chunk),
+                                       args.steps, args.warmup,
+                                       res["roofline"]["algorithmic_bytes_per_launch"])
+    res["roofline"]["traffic"] = traffic
+    if scaled_from:
+        res["roofline"]["traffic_scaled_from"] = scaled_from
     # a pool at least 1.5 times the 256 MB last-level cache: a repeated pass
     # over it evicts every line before its reuse, so the reads stream from HBM
     if not chunk and k_cache.numel() * k_cache.element_size() >= (384 << 20):
